@@ -1,0 +1,174 @@
+"""Plain CPU attention oracle (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path (the HIP library
+and its Python binding) never does, and this package imports nothing from it.
+
+Two independent evaluations of the same definition live here:
+
+* ``attention`` / ``attention_rows`` call ``attn_oracle.c`` (fp64, OpenMP,
+  one score row at a time, two-pass softmax).  Its header states the
+  definition and the passages of the pages it follows ("FlashAttention (NL)",
+  sections "Problemen met standaard attention", "Online berekening van
+  Softmax" and "Samensmelting van bewerkingen in één CUDA-kernel"; the
+  "Sparse Attention" glossary page for the local window).
+* ``bruteforce_mp`` evaluates the same definition in pure Python with mpmath
+  at 50 significant digits, materialising the whole N x N score matrix and
+  normalising exp(s) directly (no max subtraction): a different route to the
+  same numbers, for tiny inputs only.
+
+Visibility of key j to query i: ``none`` all j; ``causal`` j <= i;
+``sliding`` i - window < j <= i.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+MASKS = {"none": 0, "causal": 1, "sliding": 2}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile attn_oracle.c with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+               "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def bind(path: str):
+    """Load a compiled oracle library and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lp = ctypes.POINTER(ctypes.c_longlong)
+    ll = ctypes.c_longlong
+    lib.oracle_attn_f64.argtypes = [dp, dp, dp, ll, ll, ll, ctypes.c_double,
+                                    ctypes.c_int, ll, dp, dp]
+    lib.oracle_attn_f64.restype = ctypes.c_int
+    lib.oracle_attn_rows_f64.argtypes = [dp, lp, ll, dp, dp, ll, ll,
+                                         ctypes.c_double, ctypes.c_int, ll,
+                                         dp, dp]
+    lib.oracle_attn_rows_f64.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        _lib = bind(_LIB_PATH)
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    """Exact widening to a contiguous float64 numpy array (torch or numpy in)."""
+    if hasattr(x, "detach"):  # torch tensor: bf16/f16/f32 -> f64 is exact
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray, ctype=ctypes.c_double):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP regions use (OMP_NUM_THREADS honoured)."""
+    return int(_load().oracle_num_threads())
+
+
+def attention(q, k, v, scale: float, mask: str = "none", window: int = 0):
+    """o, lse of plain attention for inputs shaped [..., N, d] (fp64 out).
+
+    Leading dimensions (batch, heads) are independent slices.  ``lse`` is
+    the natural-log normaliser ln(sum_j exp(s_ij)) over visible j.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if not (q.shape == k.shape == v.shape) or q.ndim < 2:
+        raise ValueError("q, k, v must share one shape [..., N, d]")
+    N, d = q.shape[-2], q.shape[-1]
+    BH = int(np.prod(q.shape[:-2], dtype=np.int64)) if q.ndim > 2 else 1
+    o = np.empty(q.shape, dtype=np.float64)
+    lse = np.empty(q.shape[:-1], dtype=np.float64)
+    rc = _load().oracle_attn_f64(_ptr(q), _ptr(k), _ptr(v), BH, N, d,
+                                 float(scale), MASKS[mask], int(window),
+                                 _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise RuntimeError("oracle_attn_f64 failed (%d)" % rc)
+    return o, lse
+
+
+def attention_rows(q_rows, pos, k, v, scale: float, mask: str = "none",
+                   window: int = 0):
+    """o[R, d], lse[R] for query vectors q_rows[R, d] at positions pos[R]
+    of one (batch, head) slice with keys/values k, v of shape [N, d]."""
+    q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64))
+    R, d = q_rows.shape
+    N = k.shape[0]
+    if k.shape != (N, d) or v.shape != (N, d) or pos.shape != (R,):
+        raise ValueError("shape mismatch")
+    o = np.empty((R, d), dtype=np.float64)
+    lse = np.empty((R,), dtype=np.float64)
+    rc = _load().oracle_attn_rows_f64(_ptr(q_rows), _ptr(pos, ctypes.c_longlong),
+                                      R, _ptr(k), _ptr(v), N, d, float(scale),
+                                      MASKS[mask], int(window), _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise RuntimeError("oracle_attn_rows_f64 failed (%d)" % rc)
+    return o, lse
+
+
+def visible(i: int, j: int, mask: str, window: int) -> bool:
+    """The visibility predicate, one (query, key) pair at a time."""
+    if mask == "none":
+        return True
+    if mask == "causal":
+        return j <= i
+    return i - window < j <= i
+
+
+def bruteforce_mp(q, k, v, scale: float, mask: str = "none", window: int = 0,
+                  dps: int = 50):
+    """Pure-Python mpmath evaluation of one [N, d] slice, for tiny N and d.
+
+    Materialises S = scale * Q K^T in full, then P_ij = exp(S_ij) / sum_j
+    exp(S_ij) over visible j (masked entries have weight exactly 0), then
+    O = P V and lse_i = ln sum_j exp(S_ij).  Returns float64 arrays.
+    """
+    import mpmath
+
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    N, d = q.shape
+    with mpmath.workdps(dps):
+        sc = mpmath.mpf(float(scale))
+        Q = [[mpmath.mpf(float(x)) for x in row] for row in q]
+        K = [[mpmath.mpf(float(x)) for x in row] for row in k]
+        V = [[mpmath.mpf(float(x)) for x in row] for row in v]
+        S = [[sc * mpmath.fsum(Q[i][c] * K[j][c] for c in range(d))
+              for j in range(N)] for i in range(N)]
+        o = np.zeros((N, d))
+        lse = np.full((N,), -np.inf)
+        for i in range(N):
+            w = [mpmath.exp(S[i][j]) if visible(i, j, mask, window) else mpmath.mpf(0)
+                 for j in range(N)]
+            z = mpmath.fsum(w)
+            if z == 0:
+                continue
+            for c in range(d):
+                o[i, c] = float(mpmath.fsum(w[j] * V[j][c] for j in range(N)) / z)
+            lse[i] = float(mpmath.log(z))
+    return o, lse

@@ -1,0 +1,74 @@
+"""Seeded synthetic attention inputs, shared by the tests, the oracle side and
+the GPU side.
+
+This module holds no step of the attention computation: only workload shapes
+and the random-number recipe.  Q, K and V are i.i.d. N(0, 1): the pages'
+workloads (BERT-large at length 512, GPT-2 at 1K, Long-Range Arena at 1K-4K,
+"FlashAttention (NL)", section "Empirische resultaten") need trained models
+and datasets, so dense Gaussian inputs of the shapes below stand in for them.
+
+Recipe: ``numpy.random.default_rng(seed)``; draw q, k, v in that order with
+``standard_normal(shape, dtype=float32)``; cast to the workload dtype by
+round-to-nearest-even (torch's ``Tensor.to``).  Both sides read these exact
+bytes; widening bf16/fp16/fp32 to fp64 for the oracle is exact.
+"""
+from __future__ import annotations
+
+import hashlib
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str      # "f32" | "f16" | "bf16"
+    mask: str       # "none" | "causal" | "sliding"
+    window: int     # keys visible to a query under "sliding" (else 0)
+    scale: float
+    seed: int
+
+
+WORKLOADS = [
+    Workload("tiny_f32_n128_d64", 1, 1, 128, 64, "f32", "none", 0,
+             1.0 / math.sqrt(64), 1000),
+    Workload("gpt2s_f16_b16_h12_n1024_d64", 16, 12, 1024, 64, "f16", "none", 0,
+             1.0 / 8.0, 1001),
+    Workload("prefill_bf16_causal_b4_h16_n2048_d128", 4, 16, 2048, 128, "bf16",
+             "causal", 0, 1.0 / math.sqrt(128), 1002),
+    Workload("longctx_bf16_causal_b1_h32_n16384_d128", 1, 32, 16384, 128, "bf16",
+             "causal", 0, 1.0 / math.sqrt(128), 1003),
+    Workload("swa_bf16_w4096_b1_h32_n32768_d128", 1, 32, 32768, 128, "bf16",
+             "sliding", 4096, 1.0 / math.sqrt(128), 1004),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+HEADLINE = WORKLOADS[3]
+
+
+def make_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int):
+    """q, k, v as contiguous CPU tensors [B, H, N, d] of ``dtype``."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(3):
+        x = rng.standard_normal((B, H, N, d), dtype=np.float32)
+        out.append(torch.from_numpy(x).to(DTYPES[dtype]).contiguous())
+    return tuple(out)
+
+
+def make_workload(w: Workload):
+    return make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed)
+
+
+def sha256(t: torch.Tensor) -> str:
+    """SHA-256 of a tensor's raw bytes (records exactly what both sides read)."""
+    b = t.detach().to("cpu").contiguous().view(torch.uint8).numpy().tobytes()
+    return hashlib.sha256(b).hexdigest()
