@@ -1,0 +1,168 @@
+"""Python binding of libfa.so: the fused exact attention forward pass on
+gfx950 (MI355X).
+
+The functions named like the C ABI (``fa_fwd``, ``fa_fwd_record_tiles``,
+``fa_tile_shape``, ``fa_tile_map``, ``fa_status_string``, ``fa_last_error``,
+``fa_probe_mfma``) only marshal arguments: pointers are plain integers
+(device addresses, e.g. ``tensor.data_ptr()``), the stream is a hipStream_t
+handle (``torch.cuda.current_stream().cuda_stream``), and every step of the
+computation runs in the library's kernels.  ``attention`` is the torch-facing
+convenience: it allocates o and lse with torch on the inputs' device and
+calls ``fa_fwd`` on the current stream.
+
+There is no fallback: if libfa.so is not built, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "fa.h")
+
+FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
+FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_SLIDING = 0, 1, 2
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_NO_DEVICE, FA_ERR_HIP = range(5)
+FA_TILE_SKIP, FA_TILE_FULL, FA_TILE_PARTIAL = 0, 1, 2
+
+MASKS = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "sliding": FA_MASK_SLIDING}
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, fa_status_string(status), fa_last_error()))
+
+
+_lib = None
+
+
+def load():
+    """Load libfa.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libfa.so is not built at %s; run __graft_entry__.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_record_tiles.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, vp, vp]
+    lib.fa_fwd_record_tiles.restype = i
+    lib.fa_tile_shape.argtypes = [i, i, ip, ip, ip]
+    lib.fa_tile_shape.restype = i
+    lib.fa_tile_map.argtypes = [i, i, i, i, i, vp]
+    lib.fa_tile_map.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_probe_mfma.argtypes = [i, vp, vp, vp, vp]
+    lib.fa_probe_mfma.restype = i
+    _lib = lib
+    return lib
+
+
+def declared_functions():
+    """Names of the functions include/fa.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+# ---- raw C-ABI mirrors ------------------------------------------------------
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window, in_dtype,
+           out_dtype, stream) -> int:
+    return load().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window,
+                         in_dtype, out_dtype, stream)
+
+
+def fa_fwd_record_tiles(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window,
+                        in_dtype, out_dtype, tiles, stream) -> int:
+    return load().fa_fwd_record_tiles(q, k, v, o, lse, B, H, N, d, scale, mask_kind,
+                                      window, in_dtype, out_dtype, tiles, stream)
+
+
+def fa_tile_shape(d: int, in_dtype: int):
+    """(rows_per_workgroup, rows_per_wave, keys_per_block); raises on error."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    st = load().fa_tile_shape(d, in_dtype, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    if st != FA_OK:
+        raise FaError(st, "fa_tile_shape")
+    return a.value, b.value, c.value
+
+
+def fa_tile_map(N: int, d: int, in_dtype: int, mask_kind: int, window: int):
+    """Host tile map as a list of rows (one per row block) of FA_TILE_*."""
+    _, rw, bc = fa_tile_shape(d, in_dtype)
+    R, C = -(-N // rw), -(-N // bc)
+    buf = (ctypes.c_ubyte * (R * C))()
+    st = load().fa_tile_map(N, d, in_dtype, mask_kind, window, ctypes.cast(buf, ctypes.c_void_p))
+    if st != FA_OK:
+        raise FaError(st, "fa_tile_map")
+    flat = bytes(buf)
+    return [list(flat[r * C:(r + 1) * C]) for r in range(R)]
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(status).decode()
+
+
+def fa_last_error() -> str:
+    return load().fa_last_error().decode()
+
+
+def fa_probe_mfma(which, a, b, d, stream) -> int:
+    return load().fa_probe_mfma(which, a, b, d, stream)
+
+
+# ---- torch convenience --------------------------------------------------------
+def _dtype_code(t):
+    import torch
+    codes = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16,
+             torch.bfloat16: FA_DTYPE_BF16}
+    if t not in codes:
+        raise TypeError("unsupported dtype %s" % t)
+    return codes[t]
+
+
+def attention(q, k, v, scale=None, mask: str = "none", window: int = 0,
+              out_dtype=None, record_tiles=None):
+    """o, lse = softmax(scale q k^T + mask) v for device tensors [B, H, N, d].
+
+    ``out_dtype`` is the input dtype (default) or torch.float32.  ``lse`` is
+    float32 [B, H, N].  ``record_tiles``: optional zero-filled uint8 device
+    tensor that receives the kernel's tile decisions (see fa.h).
+    """
+    import torch
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one shape [B, H, N, d]")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous [B, H, N, d]")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    o = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            B, H, N, d, float(scale), MASKS[mask], int(window),
+            _dtype_code(q.dtype), _dtype_code(out_dtype))
+    with torch.cuda.device(q.device):
+        if record_tiles is None:
+            st = fa_fwd(*args, stream)
+        else:
+            st = fa_fwd_record_tiles(*args, record_tiles.data_ptr(), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd")
+    return o, lse

@@ -1,0 +1,224 @@
+// Host side of the C ABI declared in include/fa.h: argument checks (pure
+// host code, no HIP call before they pass), device check, grid order and
+// dispatch to the gfx950 kernels, error reporting.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/fa.h"
+#include "fa_kernels.h"
+#include "tile_class.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return FA_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
+
+bool valid_dtype(int t) {
+  return t == FA_DTYPE_F32 || t == FA_DTYPE_F16 || t == FA_DTYPE_BF16;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int keys_per_block(int in_dtype) {
+  return in_dtype == FA_DTYPE_F32 ? FA_KEYS_32 : FA_KEYS_16;
+}
+
+// Everything that can be decided without the device.
+int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int mask_kind, int window,
+               int in_dtype, int out_dtype) {
+  if (!q || !k || !v || !o || !lse)
+    return fail(FA_ERR_INVALID_ARG, "null pointer argument");
+  if (B < 1 || H < 1 || N < 1)
+    return fail(FA_ERR_INVALID_ARG, "B, H and N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if (N >= (1 << 30)) return fail(FA_ERR_INVALID_ARG, "N must be < 2^30 (got %d)", N);
+  if (!valid_dtype(in_dtype)) return fail(FA_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
+  if (!valid_dtype(out_dtype)) return fail(FA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  if (out_dtype != in_dtype && out_dtype != FA_DTYPE_F32)
+    return fail(FA_ERR_INVALID_ARG, "out_dtype must equal in_dtype or be F32");
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL && mask_kind != FA_MASK_SLIDING)
+    return fail(FA_ERR_INVALID_ARG, "unknown mask_kind %d", mask_kind);
+  if (mask_kind == FA_MASK_SLIDING && window < 1)
+    return fail(FA_ERR_INVALID_ARG, "sliding window must be >= 1 (got %d)", window);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(FA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+  const long double total = (long double)B * H * N * d;
+  if (total >= 4.611686018427387904e18L)  // 2^62
+    return fail(FA_ERR_INVALID_ARG, "B*H*N*d too large");
+  const long long bh = (long long)B * H;
+  const long long tiles = bh * ((N + FA_ROWS_PER_WG - 1) / FA_ROWS_PER_WG);
+  if (tiles > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "too many row tiles for one grid");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
+  const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u;
+  if (mis) return fail(FA_ERR_INVALID_ARG, "q, k, v, o must be 16-byte aligned");
+  if (((uintptr_t)lse & 3u) != 0) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const size_t nin = (size_t)bh * N * d * elem_bytes(in_dtype);
+  const size_t nout = (size_t)bh * N * d * elem_bytes(out_dtype);
+  const size_t nlse = (size_t)bh * N * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  for (const void* in : ins) {
+    if (overlaps(o, nout, in, nin)) return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
+    if (overlaps(lse, nlse, in, nin)) return fail(FA_ERR_INVALID_ARG, "lse overlaps an input");
+  }
+  if (overlaps(o, nout, lse, nlse)) return fail(FA_ERR_INVALID_ARG, "o overlaps lse");
+  return FA_OK;
+}
+
+// Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(FA_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_NO_DEVICE, "device index %d", dev);
+  int state = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(FA_ERR_NO_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  if (state != 1) return fail(FA_ERR_NO_DEVICE, "device %d is not gfx950", dev);
+  return FA_OK;
+}
+
+int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+            int H, int N, int d, float scale, int mask_kind, int window, int in_dtype,
+            int out_dtype, unsigned char* tiles, void* stream) {
+  int st = check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window, in_dtype,
+                      out_dtype);
+  if (st != FA_OK) return st;
+  st = check_device();
+  if (st != FA_OK) return st;
+  FaFwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.tiles = tiles;
+  p.BH = B * H;
+  p.N = N;
+  p.mask_kind = mask_kind;
+  p.window = mask_kind == FA_MASK_SLIDING ? window : 0;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  p.n_row_tiles = (N + FA_ROWS_PER_WG - 1) / FA_ROWS_PER_WG;
+  p.xcd_split = (p.BH % 8 == 0) ? 1 : 0;
+  p.heavy_first = mask_kind != FA_MASK_NONE ? 1 : 0;
+  hipError_t e = fa_launch_fwd(in_dtype, out_dtype, d, p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int N, int d, float scale, int mask_kind, int window, int in_dtype, int out_dtype,
+           void* stream) {
+  return run_fwd(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window, in_dtype, out_dtype,
+                 nullptr, stream);
+}
+
+int fa_fwd_record_tiles(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int N, int d, float scale, int mask_kind, int window,
+                        int in_dtype, int out_dtype, unsigned char* tiles, void* stream) {
+  if (!tiles) return fail(FA_ERR_INVALID_ARG, "null tiles buffer");
+  return run_fwd(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window, in_dtype, out_dtype,
+                 tiles, stream);
+}
+
+int fa_tile_shape(int d, int in_dtype, int* rows_per_workgroup, int* rows_per_wave,
+                  int* keys_per_block_out) {
+  if (!rows_per_workgroup || !rows_per_wave || !keys_per_block_out)
+    return fail(FA_ERR_INVALID_ARG, "null output pointer");
+  if (!valid_dtype(in_dtype)) return fail(FA_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
+  *rows_per_workgroup = FA_ROWS_PER_WG;
+  *rows_per_wave = FA_ROWS_PER_WAVE;
+  *keys_per_block_out = keys_per_block(in_dtype);
+  return ok();
+}
+
+int fa_tile_map(int N, int d, int in_dtype, int mask_kind, int window, unsigned char* out) {
+  if (!out) return fail(FA_ERR_INVALID_ARG, "null output pointer");
+  if (N < 1 || N >= (1 << 30)) return fail(FA_ERR_INVALID_ARG, "bad N %d", N);
+  if (!valid_dtype(in_dtype)) return fail(FA_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL && mask_kind != FA_MASK_SLIDING)
+    return fail(FA_ERR_INVALID_ARG, "unknown mask_kind %d", mask_kind);
+  if (mask_kind == FA_MASK_SLIDING && window < 1)
+    return fail(FA_ERR_INVALID_ARG, "sliding window must be >= 1 (got %d)", window);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
+  const int bc = keys_per_block(in_dtype);
+  const int R = (N + FA_ROWS_PER_WAVE - 1) / FA_ROWS_PER_WAVE;
+  const int C = (N + bc - 1) / bc;
+  for (int rb = 0; rb < R; ++rb) {
+    const int r0 = rb * FA_ROWS_PER_WAVE;
+    const int r1 = r0 + FA_ROWS_PER_WAVE < N ? r0 + FA_ROWS_PER_WAVE : N;
+    for (int kb = 0; kb < C; ++kb)
+      out[(size_t)rb * C + kb] =
+          (unsigned char)fa_classify(r0, r1, kb * bc, bc, N, mask_kind, window);
+  }
+  return ok();
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_NO_DEVICE: return "FA_ERR_NO_DEVICE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    default: return "FA_ERR_UNKNOWN";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+int fa_probe_mfma(int which, const void* a, const void* b, float* d, void* stream) {
+  if (which < 0 || which > 2) return fail(FA_ERR_INVALID_ARG, "which must be 0, 1 or 2");
+  if (!a || !b || !d) return fail(FA_ERR_INVALID_ARG, "null pointer argument");
+  if ((((uintptr_t)a | (uintptr_t)b) & 15u) != 0 || ((uintptr_t)d & 3u) != 0)
+    return fail(FA_ERR_INVALID_ARG, "misaligned operand");
+  int st = check_device();
+  if (st != FA_OK) return st;
+  hipError_t e = fa_launch_probe(which, a, b, d, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// Internal interface between the host API (fa_api.cpp) and the gfx950
+// kernels (fa_fwd.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+struct FaFwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  unsigned char* tiles;   // optional tile-decision record (nullptr: off)
+  int BH;                 // batch * heads
+  int N;                  // sequence length
+  int mask_kind;          // FA_MASKK_*
+  int window;             // sliding window (keys), >= 1 when sliding
+  float scale_log2;       // scale * log2(e)
+  int n_row_tiles;        // ceil(N / rows_per_workgroup)
+  int xcd_split;          // 1: give each XCD its own heads (BH % 8 == 0)
+  int heavy_first;        // 1: longest row tiles launched first (masks)
+};
+
+// Tile geometry per input precision.
+constexpr int FA_WAVES = 4;              // wavefronts per workgroup
+constexpr int FA_ROWS_PER_WAVE = 32;     // query rows owned by one wavefront
+constexpr int FA_ROWS_PER_WG = FA_WAVES * FA_ROWS_PER_WAVE;
+constexpr int FA_KEYS_16 = 64;           // keys per K/V block, f16/bf16
+constexpr int FA_KEYS_32 = 32;           // keys per K/V block, f32
+
+// dtype codes as in fa.h
+hipError_t fa_launch_fwd(int in_dtype, int out_dtype, int d,
+                         const FaFwdParams& p, hipStream_t stream);
+hipError_t fa_launch_probe(int which, const void* a, const void* b, float* d,
+                           hipStream_t stream);

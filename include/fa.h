@@ -1,0 +1,142 @@
+/*
+ * fa.h -- C ABI of the fused exact attention forward library (libfa.so),
+ * gfx950 (MI355X) only.
+ *
+ * What is computed.  "FlashAttention (NL)", section "Problemen met standaard
+ * attention", defines attention as softmax(Q K^T / sqrt(d_k)) V.  Sections
+ * "Tiling en blokgewijze verwerking", "Online berekening van Softmax" and
+ * "Samensmelting van bewerkingen in één CUDA-kernel" of the same page give
+ * the method: Q, K, V are processed in blocks held in on-chip memory, a
+ * running row maximum and a running sum of exponentials make the blockwise
+ * softmax exact, and QK^T, masking, softmax and the product with V run in one
+ * fused kernel that writes only the final result, so the N x N score matrix
+ * never reaches device memory.  For every (b, h, i):
+ *
+ *   s_ij     = scale * <q[b,h,i,:], k[b,h,j,:]>      for visible j
+ *   o[b,h,i] = sum_j exp(s_ij) v[b,h,j,:] / sum_j exp(s_ij)
+ *   lse[b,h,i] = ln sum_j exp(s_ij)       (natural log, always fp32)
+ *
+ * lse is the online-softmax pair (running maximum m, exponent sum l) folded
+ * into one number, m + ln l; it is what a backward pass would recompute the
+ * probabilities from.
+ *
+ * Visibility of key j to query i (mask_kind):
+ *   FA_MASK_NONE     every j in [0, N)
+ *   FA_MASK_CAUSAL   j <= i
+ *   FA_MASK_SLIDING  i - window < j <= i: the `window` most recent keys
+ *                    including the query's own position (the local window of
+ *                    the "Sparse Attention" glossary page, "Abgrenzung &
+ *                    Vergleiche").  window >= N is the causal mask.
+ *
+ * Layout.  q, k, v, o: contiguous row-major [B][H][N][d] (d innermost).
+ * lse: contiguous [B][H][N] float.  All pointers are device pointers (for
+ * example from PyTorch), 16-byte aligned; outputs must not overlap inputs.
+ *
+ * Ownership and memory.  The caller owns every buffer.  The library
+ * allocates no device memory and keeps no workspace: apart from o and lse
+ * nothing of size O(N) or O(N^2) is written ("Complexiteit en optimaliteit":
+ * memory O(N) instead of O(N^2)).
+ *
+ * Streams.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns once it is enqueued: outputs are valid after
+ * the stream is synchronised.  The only global state is per-thread error
+ * text, so calls from several host threads are safe.
+ *
+ * Errors.  Nothing is thrown or aborted across the ABI.  Arguments are
+ * checked on the host before any HIP call, so a bad argument returns
+ * FA_ERR_INVALID_ARG or FA_ERR_UNSUPPORTED without touching the device.  A
+ * HIP failure returns FA_ERR_HIP (or FA_ERR_NO_DEVICE) and fa_last_error()
+ * holds the runtime's text.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { FA_DTYPE_F32 = 0, FA_DTYPE_F16 = 1, FA_DTYPE_BF16 = 2 };
+enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_SLIDING = 2 };
+enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad enum, misalignment */
+  FA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement   */
+  FA_ERR_NO_DEVICE = 3,   /* no usable gfx950 device                        */
+  FA_ERR_HIP = 4          /* the HIP runtime reported an error              */
+};
+
+/*
+ * Fused attention forward (the operation above).
+ *   q, k, v    [B][H][N][d] of in_dtype
+ *   o          [B][H][N][d] of out_dtype (out_dtype == in_dtype, or F32)
+ *   lse        [B][H][N] float
+ *   B, H, N    >= 1, with B*H*N*d < 2^62 and N < 2^30
+ *   d          64 or 128 (else FA_ERR_UNSUPPORTED)
+ *   scale      finite and >= 0 (1/sqrt(d) in the page's formula; 0 gives
+ *              uniform weights over the visible keys)
+ *   mask_kind  FA_MASK_*; window >= 1 when FA_MASK_SLIDING, ignored otherwise
+ *   in_dtype   FA_DTYPE_F32, FA_DTYPE_F16 or FA_DTYPE_BF16
+ *   out_dtype  in_dtype or FA_DTYPE_F32 (F32 inputs need F32 output)
+ *   stream     hipStream_t or NULL
+ * Arithmetic: products on the matrix cores in the input precision with fp32
+ * accumulation; softmax statistics in fp32; probabilities are rounded to the
+ * input precision (round to nearest even) before the product with V.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int mask_kind, int window,
+           int in_dtype, int out_dtype, void* stream);
+
+/*
+ * Same as fa_fwd, and records the tile decisions the kernel took: for every
+ * (b, h), row block rb of tile_rows rows and key block kb of tile_keys keys
+ * (see fa_tile_shape), tiles[((b*H + h) * R + rb) * C + kb] is set to
+ * FA_TILE_* + 1 (1 skipped, 2 full, 3 partial) by the wave that owns the
+ * row block, with R = ceil(N / tile_rows) and C = ceil(N / tile_keys).  The
+ * caller zero-fills `tiles` (B*H*R*C bytes, device memory) beforehand;
+ * entries of key blocks outside the workgroup's visited range stay 0.  A
+ * diagnostic for the tile-skip structure; not for timing.
+ */
+int fa_fwd_record_tiles(const void* q, const void* k, const void* v, void* o,
+                        float* lse, int B, int H, int N, int d, float scale,
+                        int mask_kind, int window, int in_dtype, int out_dtype,
+                        unsigned char* tiles, void* stream);
+
+/*
+ * Tile geometry the dispatcher uses for (d, in_dtype): rows handled by one
+ * workgroup, rows handled by one wavefront (the granularity at which work is
+ * skipped), and keys per K/V block.  Host only; no device call.
+ */
+int fa_tile_shape(int d, int in_dtype, int* rows_per_workgroup,
+                  int* rows_per_wave, int* keys_per_block);
+
+/*
+ * Host-side tile map for (N, d, in_dtype, mask_kind, window): out[rb * C + kb]
+ * = FA_TILE_SKIP / FA_TILE_FULL / FA_TILE_PARTIAL (0 / 1 / 2) for row block
+ * rb (rows_per_wave rows) and key block kb (keys_per_block keys), R x C as in
+ * fa_fwd_record_tiles.  `out` is host memory of R*C bytes.  No device call.
+ */
+int fa_tile_map(int N, int d, int in_dtype, int mask_kind, int window,
+                unsigned char* out);
+
+/* Name of a status code ("FA_OK", ...).  Static storage. */
+const char* fa_status_string(int status);
+
+/* Detail text of the last failing call on this host thread ("" if none). */
+const char* fa_last_error(void);
+
+/*
+ * Diagnostic: one 32x32 output block of a matrix-core product, to check the
+ * operand and accumulator lane layouts the kernels rely on.  which = 0:
+ * bf16 32x32x16; 1: f16 32x32x16; 2: f32 32x32x2.  a and b are device
+ * pointers to 64 lanes x (8 for which 0/1, 1 for which 2) elements in lane
+ * order, d a device pointer to 64 lanes x 16 floats in lane order.  The
+ * kernel is launched on `stream` with one wavefront.
+ */
+int fa_probe_mfma(int which, const void* a, const void* b, float* d,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

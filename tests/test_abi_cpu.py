@@ -1,0 +1,126 @@
+"""The C-ABI library on the host: it loads, exports what include/fa.h
+declares, and rejects bad arguments before touching the device.
+
+Runs without a GPU.  Fake device addresses are plain integers that the
+library only compares and never dereferences: every call here either fails
+argument validation (pure host code) or stops at the device check.
+"""
+import ctypes
+
+import pytest
+
+import exact_io_aware_04_amd as fa
+
+A = 1 << 20  # fake, 16-byte aligned "device" addresses, far apart
+Q, K, V, O, L = A, 64 * A, 128 * A, 192 * A, 256 * A
+
+
+def call(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=100, d=128, scale=0.1,
+                mask_kind=fa.FA_MASK_CAUSAL, window=0, in_dtype=fa.FA_DTYPE_BF16,
+                out_dtype=fa.FA_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                     args["H"], args["N"], args["d"], args["scale"], args["mask_kind"],
+                     args["window"], args["in_dtype"], args["out_dtype"], args["stream"])
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = fa.load()
+    names = fa.declared_functions()
+    assert {"fa_fwd", "fa_fwd_record_tiles", "fa_tile_shape", "fa_tile_map",
+            "fa_status_string", "fa_last_error", "fa_probe_mfma"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    # and they really are C symbols of the shared object
+    so = ctypes.CDLL(fa.LIB_PATH)
+    for n in names:
+        assert ctypes.cast(getattr(so, n), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    assert fa.fa_status_string(fa.FA_OK) == "FA_OK"
+    assert fa.fa_status_string(fa.FA_ERR_INVALID_ARG) == "FA_ERR_INVALID_ARG"
+    assert fa.fa_status_string(fa.FA_ERR_UNSUPPORTED) == "FA_ERR_UNSUPPORTED"
+    assert fa.fa_status_string(fa.FA_ERR_NO_DEVICE) == "FA_ERR_NO_DEVICE"
+    assert fa.fa_status_string(fa.FA_ERR_HIP) == "FA_ERR_HIP"
+    assert fa.fa_status_string(99) == "FA_ERR_UNKNOWN"
+
+
+INVALID = [
+    dict(q=0), dict(k=0), dict(v=0), dict(o=0), dict(lse=0),
+    dict(B=0), dict(H=0), dict(N=0), dict(N=-5), dict(N=1 << 30), dict(d=0),
+    dict(in_dtype=7), dict(out_dtype=-1),
+    dict(in_dtype=fa.FA_DTYPE_BF16, out_dtype=fa.FA_DTYPE_F16),
+    dict(in_dtype=fa.FA_DTYPE_F32, out_dtype=fa.FA_DTYPE_BF16),
+    dict(mask_kind=3), dict(mask_kind=fa.FA_MASK_SLIDING, window=0),
+    dict(mask_kind=fa.FA_MASK_SLIDING, window=-3),
+    dict(scale=float("nan")), dict(scale=float("inf")), dict(scale=-0.5),
+    dict(q=Q + 8), dict(o=O + 2), dict(lse=L + 2),
+    dict(o=Q + 64),             # output overlaps an input
+    dict(lse=V + 1024),         # lse overlaps an input
+    dict(lse=O + 4096),         # lse overlaps o
+    dict(B=1 << 20, H=1 << 20, N=1 << 29, d=128),  # size overflow
+]
+
+
+@pytest.mark.parametrize("kw", INVALID, ids=[str(k) for k in INVALID])
+def test_invalid_arguments_are_rejected_on_the_host(kw):
+    st = call(**kw)
+    assert st == fa.FA_ERR_INVALID_ARG, (kw, fa.fa_status_string(st))
+    assert fa.fa_last_error() != ""
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_unbuilt_head_dims_are_unsupported(d):
+    assert call(d=d) == fa.FA_ERR_UNSUPPORTED
+    with pytest.raises(fa.FaError):
+        fa.fa_tile_shape(d, fa.FA_DTYPE_BF16)
+
+
+def test_valid_arguments_reach_the_device_check():
+    # no GPU in this container: a fully valid call stops at the device check
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    st = call()
+    assert st in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
+    assert fa.fa_last_error() != ""
+    st = call(mask_kind=fa.FA_MASK_SLIDING, window=1, in_dtype=fa.FA_DTYPE_F32,
+              out_dtype=fa.FA_DTYPE_F32, d=64)
+    assert st in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
+
+
+def test_record_tiles_needs_a_buffer():
+    st = fa.fa_fwd_record_tiles(Q, K, V, O, L, 1, 1, 100, 128, 0.1, 1, 0, 2, 2, None, None)
+    assert st == fa.FA_ERR_INVALID_ARG
+
+
+def test_probe_rejects_bad_arguments():
+    assert fa.fa_probe_mfma(3, Q, K, O, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_probe_mfma(0, 0, K, O, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_probe_mfma(0, Q + 4, K, O, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_tile_shape():
+    assert fa.fa_tile_shape(128, fa.FA_DTYPE_BF16) == (128, 32, 64)
+    assert fa.fa_tile_shape(64, fa.FA_DTYPE_F16) == (128, 32, 64)
+    assert fa.fa_tile_shape(64, fa.FA_DTYPE_F32) == (128, 32, 32)
+
+
+def test_tile_map_rejects_bad_arguments():
+    buf = (ctypes.c_ubyte * 16)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    lib = fa.load()
+    assert lib.fa_tile_map(0, 128, 2, 0, 0, p) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_tile_map(10, 128, 2, 2, 0, p) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_tile_map(10, 128, 2, 5, 0, p) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_tile_map(10, 100, 2, 0, 0, p) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_tile_map(10, 128, 2, 0, 0, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_torch_wrapper_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        fa.attention(x, x, x)

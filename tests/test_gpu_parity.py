@@ -1,0 +1,340 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+* matrix-core lane layouts the kernels rely on (exact integer products);
+* the five workloads (seeded N(0,1) inputs): whole-tensor parity where the
+  oracle finishes in seconds, sampled rows at the long-context sizes, in
+  the launch configuration the benchmark times;
+* ragged and tiny N, both head dims, every dtype and mask;
+* the mask / tile-skip structure exactly (position-decoding probe and the
+  kernel's own tile record against a brute-force map);
+* closed forms (constant V, zero scale, window 1, window >= N) and
+  invariants (determinism, batch slicing) on the device.
+Tolerances: O max-abs <= 1e-5 (fp32 inputs) / 1e-2 (bf16, fp16; plus half
+an ulp of the output dtype when O is stored in it); lse <= 1e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_04_amd as fa
+import oracle
+import seeded_inputs as si
+from tests.parity_util import (compare, decode_positions, expected_range,
+                               position_inputs, say)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load()
+    yield
+
+
+def run(q, k, v, scale, mask="none", window=0, out_dtype=None):
+    o, lse = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV), scale, mask, window, out_dtype)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# matrix-core lane layouts
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_mfma_lane_layout(which):
+    """A[m][k] in lane m%32 / slot (lane/32, i); B[k][n] in lane n%32;
+    D[m][n] in lane n + 32*((m/4)%2), register 4*(m/8) + m%4."""
+    say("mfma probe", which)
+    kdim = 2 if which == 2 else 16
+    per = 1 if which == 2 else 8
+    rng = np.random.default_rng(5 + which)
+    A = rng.integers(-3, 4, size=(32, kdim)).astype(np.float32)
+    Bm = rng.integers(-3, 4, size=(kdim, 32)).astype(np.float32)
+    a_l = np.zeros((64, per), np.float32)
+    b_l = np.zeros((64, per), np.float32)
+    for lane in range(64):
+        for i in range(per):
+            kk = (lane // 32) * per + i
+            a_l[lane, i] = A[lane % 32, kk]
+            b_l[lane, i] = Bm[kk, lane % 32]
+    dt = {0: torch.bfloat16, 1: torch.float16, 2: torch.float32}[which]
+    a = torch.from_numpy(a_l).to(dt).to(DEV)
+    b = torch.from_numpy(b_l).to(dt).to(DEV)
+    d = torch.zeros(64 * 16, dtype=torch.float32, device=DEV)
+    st = fa.fa_probe_mfma(which, a.data_ptr(), b.data_ptr(), d.data_ptr(),
+                          torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_OK, fa.fa_last_error()
+    torch.cuda.synchronize()
+    d = d.cpu().numpy().reshape(64, 16)
+    want = A.astype(np.float64) @ Bm.astype(np.float64)
+    got = np.zeros((32, 32))
+    for lane in range(64):
+        for r in range(16):
+            m = 8 * (r // 4) + 4 * (lane // 32) + r % 4
+            got[m, lane % 32] = d[lane, r]
+    np.testing.assert_array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------
+# the workloads
+# ---------------------------------------------------------------------------
+SMALL = [w for w in si.WORKLOADS if w.B * w.H * w.N <= 300_000]
+LARGE = [w for w in si.WORKLOADS if w.B * w.H * w.N > 300_000]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_workload_whole_tensor(w):
+    say("workload whole", w.name)
+    q, k, v = si.make_workload(w)
+    o_ref, lse_ref = oracle.attention(q, k, v, w.scale, w.mask, w.window)
+    dt = DT[w.dtype]
+    o, lse = run(q, k, v, w.scale, w.mask, w.window, torch.float32)
+    compare(o, lse, o_ref, lse_ref, dt, w.name + " fp32-out")
+    if dt != torch.float32:
+        o, lse = run(q, k, v, w.scale, w.mask, w.window)
+        assert o.dtype == dt
+        compare(o, lse, o_ref, lse_ref, dt, w.name + " dtype-out")
+
+
+def sample_rows(N, rng, extra=64):
+    fixed = list(range(0, 64)) + [127, 128, 129, 4095, 4096, 4097, N // 2, N // 2 + 1]
+    fixed += list(range(N - 64, N))
+    rnd = rng.integers(0, N, size=extra).tolist()
+    return np.array(sorted({r for r in fixed + rnd if 0 <= r < N}), dtype=np.int64)
+
+
+@pytest.mark.parametrize("w", LARGE, ids=[w.name for w in LARGE])
+def test_workload_sampled_rows(w):
+    """Full-size launch (the benchmark's configuration); sampled rows of three
+    heads checked one by one against the oracle."""
+    say("workload sampled", w.name)
+    q, k, v = si.make_workload(w)
+    dt = DT[w.dtype]
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o32, lse32 = fa.attention(qd, kd, vd, w.scale, w.mask, w.window, torch.float32)
+    o16, lse16 = fa.attention(qd, kd, vd, w.scale, w.mask, w.window)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o16).all() and torch.isfinite(lse16).all()
+    rng = np.random.default_rng(w.seed)
+    bhs = sorted({(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2)})
+    for b, h in bhs:
+        rows = sample_rows(w.N, rng)
+        o_ref, lse_ref = oracle.attention_rows(q[b, h][rows], rows, k[b, h], v[b, h],
+                                               w.scale, w.mask, w.window)
+        idx = torch.from_numpy(rows).to(DEV)
+        compare(o32[b, h].index_select(0, idx), lse32[b, h].index_select(0, idx),
+                o_ref, lse_ref, dt, "%s b%d h%d fp32-out" % (w.name, b, h))
+        compare(o16[b, h].index_select(0, idx), lse16[b, h].index_select(0, idx),
+                o_ref, lse_ref, dt, "%s b%d h%d dtype-out" % (w.name, b, h))
+
+
+# ---------------------------------------------------------------------------
+# ragged / tiny sizes, both head dims, every dtype and mask
+# ---------------------------------------------------------------------------
+RAGGED_N = [1, 2, 7, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 257, 1000]
+MASKS = [("none", 0), ("causal", 0), ("sliding", 1), ("sliding", 33), ("sliding", 100)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask,window", MASKS)
+def test_ragged_sizes(dtype, d, mask, window):
+    dt = DT[dtype]
+    for N in RAGGED_N:
+        say("ragged", dtype, d, mask, window, N)
+        q, k, v = si.make_qkv(2, 3, N, d, dtype, 7000 + N + d)
+        scale = 1.0 / math.sqrt(d)
+        o_ref, lse_ref = oracle.attention(q, k, v, scale, mask, window)
+        o, lse = run(q, k, v, scale, mask, window, torch.float32)
+        compare(o, lse, o_ref, lse_ref, dt, "N=%d fp32-out" % N)
+        if dt != torch.float32:
+            o, lse = run(q, k, v, scale, mask, window)
+            compare(o, lse, o_ref, lse_ref, dt, "N=%d dtype-out" % N)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_large_logits_stress(dtype):
+    """Logit std 4 and 8: the running maximum moves often, many exps
+    underflow."""
+    dt = DT[dtype]
+    for mult in (4.0, 8.0):
+        say("stress", dtype, mult)
+        q, k, v = si.make_qkv(1, 4, 700, 128, dtype, 42)
+        q = (q.float() * mult).to(dt)
+        scale = 1.0 / math.sqrt(128)
+        for mask, window in (("none", 0), ("causal", 0), ("sliding", 77)):
+            o_ref, lse_ref = oracle.attention(q, k, v, scale, mask, window)
+            o, lse = run(q, k, v, scale, mask, window, torch.float32)
+            compare(o, lse, o_ref, lse_ref, dt, "stress x%g %s" % (mult, mask))
+
+
+# ---------------------------------------------------------------------------
+# mask and tile-skip structure, exactly
+# ---------------------------------------------------------------------------
+PROBE = [(2048, "causal", 0), (2047, "causal", 0), (3000, "sliding", 4096),
+         (3000, "sliding", 700), (2113, "sliding", 64), (1500, "none", 0),
+         (16384, "causal", 0), (32768, "sliding", 4096), (16383, "sliding", 4095)]
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("bf16", 64), ("f32", 64)])
+@pytest.mark.parametrize("N,mask,window", PROBE)
+def test_position_probe_recovers_visible_range(dtype, d, N, mask, window):
+    if dtype == "f32" and N > 4096:
+        pytest.skip("fp32 probe kept to small N")
+    dt = DT[dtype]
+    lo_want, hi_want = expected_range(N, mask, window)
+    for reverse in (False, True):
+        say("position probe", dtype, d, N, mask, window, reverse)
+        q, k, v, scale, nbits = position_inputs(N, d, dt, reverse)
+        o, _ = run(q, k, v, scale, mask, window, torch.float32)
+        pos, dev = decode_positions(o[0, 0], nbits)
+        assert dev < 1e-3, "output digits not 0/1 (max dev %g)" % dev
+        want = lo_want if reverse else hi_want
+        bad = np.nonzero(pos != want)[0]
+        assert bad.size == 0, "rows %s decode %s, want %s" % (bad[:5], pos[bad[:5]], want[bad[:5]])
+
+
+def brute_tiles(N, rows, keys, mask, window):
+    i = np.arange(N)[:, None]
+    C = -(-N // keys)
+    j = np.arange(C * keys)[None, :]
+    vis = np.ones((N, C * keys), bool) if mask == "none" else (j <= i)
+    if mask == "sliding":
+        vis &= j > i - window
+    vis &= j < N
+    R = -(-N // rows)
+    out = np.zeros((R, C), np.uint8)
+    for rb in range(R):
+        for kb in range(C):
+            blk = vis[rb * rows:(rb + 1) * rows, kb * keys:(kb + 1) * keys]
+            out[rb, kb] = 0 if not blk.any() else (1 if blk.all() else 2)
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N,mask,window", [(1000, "causal", 0), (1000, "sliding", 130),
+                                           (777, "none", 0), (4096, "sliding", 1),
+                                           (4096, "causal", 0), (129, "sliding", 64)])
+def test_kernel_tile_decisions(dtype, N, mask, window):
+    """The kernel's own record of skipped / full / partial blocks equals the
+    brute-force map; key blocks outside a workgroup's range are never
+    visited."""
+    say("tile record", dtype, N, mask, window)
+    dt = DT[dtype]
+    wg_rows, rows, keys = fa.fa_tile_shape(128, fa._dtype_code(dt))
+    B, H = 2, 2
+    q, k, v = si.make_qkv(B, H, N, 128, dtype, 99)
+    R, C = -(-N // rows), -(-N // keys)
+    rec = torch.zeros(B * H * R * C, dtype=torch.uint8, device=DEV)
+    o, lse = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV), 0.1, mask, window,
+                          torch.float32, record_tiles=rec)
+    torch.cuda.synchronize()
+    rec = rec.cpu().numpy().reshape(B * H, R, C)
+    want_wave = brute_tiles(N, rows, keys, mask, window)
+    want_wg = brute_tiles(N, wg_rows, keys, mask, window)
+    for bh in range(B * H):
+        for rb in range(R):
+            wg = want_wg[rb * rows // wg_rows]
+            visited = np.nonzero(wg)[0]
+            lo, hi = visited.min(), visited.max() + 1
+            expect = np.zeros(C, np.uint8)
+            expect[lo:hi] = want_wave[rb, lo:hi] + 1
+            np.testing.assert_array_equal(rec[bh, rb], expect, err_msg="bh %d rb %d" % (bh, rb))
+    o_ref, lse_ref = oracle.attention(q, k, v, 0.1, mask, window)
+    compare(o, lse, o_ref, lse_ref, dt, "tile record run")
+
+
+# ---------------------------------------------------------------------------
+# closed forms and invariants on the device
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("f32", 128)])
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 300)])
+def test_constant_values_and_zero_scale(dtype, d, mask, window):
+    dt = DT[dtype]
+    N = 1111
+    q, k, v = si.make_qkv(1, 2, N, d, dtype, 123)
+    # constant V: every output row equals that constant
+    c = torch.linspace(-3, 3, d).to(dt)
+    vc = c.expand(1, 2, N, d).contiguous()
+    say("constant V", dtype, d, mask)
+    o, _ = run(q, k, vc, 1.0 / math.sqrt(d), mask, window, torch.float32)
+    tol = 1e-5 if dt == torch.float32 else 1e-2
+    assert (o.cpu().double() - c.double()).abs().max().item() <= tol
+    # scale 0: uniform weights, lse = ln(number of visible keys)
+    say("zero scale", dtype, d, mask)
+    o, lse = run(q, k, v, 0.0, mask, window, torch.float32)
+    lo, hi = expected_range(N, mask, window)
+    cnt = hi - lo + 1
+    vv = v[0].double().numpy()
+    cs = np.concatenate([np.zeros((2, 1, d)), np.cumsum(vv, axis=1)], axis=1)
+    mean = (cs[:, hi + 1] - cs[:, lo]) / cnt[None, :, None]
+    compare(o[0], lse[0], mean, np.broadcast_to(np.log(cnt), (2, N)), dt, "zero scale")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_window_special_cases(dtype):
+    dt = DT[dtype]
+    N, d = 1300, 64
+    q, k, v = si.make_qkv(1, 2, N, d, dtype, 321)
+    say("window 1", dtype)
+    o, lse = run(q, k, v, 0.125, "sliding", 1, torch.float32)
+    s_ii = 0.125 * (q.double() * k.double()).sum(-1)
+    compare(o, lse, v.double().numpy(), s_ii.numpy(), dt, "window 1")
+    say("window >= N", dtype)
+    oc, lc = run(q, k, v, 0.125, "causal", 0)
+    for w in (N, N + 1, 1 << 30):
+        ow, lw = run(q, k, v, 0.125, "sliding", w)
+        assert torch.equal(ow, oc) and torch.equal(lw, lc)
+
+
+def test_determinism_and_slicing():
+    B, H, N, d = 2, 4, 1000, 128
+    q, k, v = si.make_qkv(B, H, N, d, "bf16", 55)
+    say("determinism")
+    o1, l1 = run(q, k, v, 0.09, "causal")
+    o2, l2 = run(q, k, v, 0.09, "causal")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    say("slicing")
+    for b in range(B):
+        for h in range(H):
+            sl = lambda t: t[b:b + 1, h:h + 1].contiguous()
+            os_, ls_ = run(sl(q), sl(k), sl(v), 0.09, "causal")
+            assert torch.equal(os_[0, 0], o1[b, h]) and torch.equal(ls_[0, 0], l1[b, h])
+
+
+def test_no_device_workspace():
+    """Nothing beyond o and lse is allocated: device free memory is unchanged
+    across a call (after a first call has loaded the code object)."""
+    q, k, v = (t.to(DEV) for t in si.make_qkv(1, 8, 4096, 128, "bf16", 77))
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 8, 4096), dtype=torch.float32, device=DEV)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            1, 8, 4096, 128, 0.088, fa.FA_MASK_CAUSAL, 0, fa.FA_DTYPE_BF16, fa.FA_DTYPE_BF16,
+            torch.cuda.current_stream().cuda_stream)
+    say("workspace")
+    assert fa.fa_fwd(*args) == fa.FA_OK
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    alloc0 = torch.cuda.memory_allocated()
+    for _ in range(3):
+        assert fa.fa_fwd(*args) == fa.FA_OK
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0 and torch.cuda.memory_allocated() == alloc0
+
+
+def test_errors_on_device():
+    q = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(fa.FaError) as e:
+        fa.attention(q, q, q)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(fa.FaError) as e:
+        fa.attention(q, q, q, mask="sliding", window=0)
+    assert e.value.status == fa.FA_ERR_INVALID_ARG
