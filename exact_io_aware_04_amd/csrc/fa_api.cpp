@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cstdarg>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -133,8 +134,15 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   p.BH = B * H;
   p.N = N;
   p.mask_kind = mask_kind;
-  p.window = mask_kind == FA_MASK_SLIDING ? window : 0;
+  // a window of N or more keys is the causal mask; clamping keeps every
+  // index computation of the kernels far from int overflow
+  p.window = mask_kind == FA_MASK_SLIDING ? (window < N ? window : N) : 0;
+  // The kernel needs scale_log2 > 0 (masked scores are -inf and must map to
+  // probability 0).  scale = 0 becomes the smallest normal float: every
+  // exponent s*scale_log2 is then below 2^-100 in magnitude, so each weight
+  // is 1 to fp32 precision -- the uniform weights scale = 0 defines.
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  if (!(p.scale_log2 >= FLT_MIN)) p.scale_log2 = FLT_MIN;
   p.n_row_tiles = (N + FA_ROWS_PER_WG - 1) / FA_ROWS_PER_WG;
   p.xcd_split = (p.BH % 8 == 0) ? 1 : 0;
   p.heavy_first = mask_kind != FA_MASK_NONE ? 1 : 0;

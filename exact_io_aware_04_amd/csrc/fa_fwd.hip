@@ -99,6 +99,20 @@ __device__ __forceinline__ fa_u32x2 pack4(float a, float b, float c, float d) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + lo + hi of a packed pair of 16-bit values (one v_dot2c with (1, 1)).
+template <int DT>
+__device__ __forceinline__ float sum2(unsigned int pair, float acc) {
+  if constexpr (DT == 2) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+  } else {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // geometry
 // ---------------------------------------------------------------------------
@@ -176,16 +190,16 @@ fa_fwd_kernel(FaFwdParams p) {
   constexpr int NQF = G::F32 ? D / 2 : D / 16;
   fa_u32x4 qf16[G::F32 ? 1 : NQF];
   float qf32[G::F32 ? NQF : 1];
+  // Rows past N read row N-1 instead (no branch); their results are never
+  // stored.
+  const size_t qrow = (size_t)min(qi, N - 1) * D;
   if constexpr (G::F32) {
 #pragma unroll
-    for (int ks = 0; ks < NQF; ++ks)
-      qf32[ks] = qi < N ? ((const float*)Qb)[(size_t)qi * D + 2 * ks + half] : 0.f;
+    for (int ks = 0; ks < NQF; ++ks) qf32[ks] = ((const float*)Qb)[qrow + 2 * ks + half];
   } else {
 #pragma unroll
-    for (int ks = 0; ks < NQF; ++ks) {
-      fa_u32x4 z = {0u, 0u, 0u, 0u};
-      qf16[ks] = qi < N ? *(const fa_u32x4*)(Qb + ((size_t)qi * D + ks * 16 + half * 8) * 2) : z;
-    }
+    for (int ks = 0; ks < NQF; ++ks)
+      qf16[ks] = *(const fa_u32x4*)(Qb + (qrow + ks * 16 + half * 8) * 2);
   }
 
   // ---- K/V staging -------------------------------------------------------
@@ -193,15 +207,17 @@ fa_fwd_kernel(FaFwdParams p) {
   const int jg = tid / G::CPR;  // row group: rows jg*LPT .. jg*LPT+LPT-1
   fa_u32x4 kst[G::LPT], vst[G::LPT];
 
+  // Keys past N load row N-1 (no branch): such keys only occur in boundary
+  // blocks, where the mask gives them probability exactly 0, and the finite
+  // values loaded there contribute 0 * v = 0 to the product with V.
   auto gload = [&](int kt) {
     const int k0 = kt * BC;
 #pragma unroll
     for (int r = 0; r < G::LPT; ++r) {
-      const int j = k0 + jg * G::LPT + r;
-      fa_u32x4 z = {0u, 0u, 0u, 0u};
+      const int j = min(k0 + jg * G::LPT + r, N - 1);
       const size_t off = ((size_t)j * D + cc * G::EPC) * G::ESZ;
-      kst[r] = j < N ? *(const fa_u32x4*)(Kb + off) : z;
-      vst[r] = j < N ? *(const fa_u32x4*)(Vb + off) : z;
+      kst[r] = *(const fa_u32x4*)(Kb + off);
+      vst[r] = *(const fa_u32x4*)(Vb + off);
     }
   };
 
@@ -247,28 +263,31 @@ fa_fwd_kernel(FaFwdParams p) {
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
   float m_ref = FA_NEG_INF;  // reference maximum (base-2 scaled units)
   float l_lane = 0.f;        // this lane's part of the exponent sum
+  float lq_lane = 0.f;       // same, of the probabilities as rounded for P V
   const float c2 = p.scale_log2;
 
   const int n_row_blocks = (N + FA_ROWS_PER_WAVE - 1) / FA_ROWS_PER_WAVE;
   const int n_key_blocks = (N + BC - 1) / BC;
   const int row_block = qw0 / FA_ROWS_PER_WAVE;
 
-  if (kv_lo < kv_hi) {
-    gload(kv_lo);
-    lstore(0);
-  }
+  // Every workgroup has at least one key block: row q0 < N always sees key
+  // q0 itself (the diagonal is visible under every mask).
+  gload(kv_lo);
+  lstore(0);
+  // All loads issued so far (Q fragments included) have landed: the loop's
+  // prefetch of the next block then never has to wait behind them.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int kt = kv_lo; kt < kv_hi; ++kt) {
     const int buf = (kt - kv_lo) & 1;
     const bool has_next = kt + 1 < kv_hi;
-    if (has_next) gload(kt + 1);
-
     const int k0 = kt * BC;
     const int cls = fa_classify(qw0, qw1, k0, BC, N, p.mask_kind, p.window);
     if (p.tiles && lane == 0 && qw0 < N)
       p.tiles[((size_t)bh * n_row_blocks + row_block) * n_key_blocks + kt] =
           (unsigned char)(cls + 1);
+    if (has_next) gload(kt + 1);
 
     if (cls != FA_TILE_SKIP) {
       const unsigned char* kbuf = smem + buf * G::KBYTES;
@@ -295,29 +314,31 @@ fa_fwd_kernel(FaFwdParams p) {
         }
       }
 
-      // ---- mask (boundary blocks only) and row maximum
-      unsigned int vis = 0xffffffffu;  // bit 16kb + r: pair visible
+      // ---- mask (boundary blocks only): invisible scores become -inf, which
+      // the exponential below maps to exactly 0 (scale_log2 > 0)
       if (cls == FA_TILE_PARTIAL) {
-        vis = 0u;
+        // row qi sees keys jlo..jhi; key j is visible iff 0 <= j-jlo <= span
+        const int jhi = p.mask_kind == FA_MASKK_NONE ? N - 1 : min(qi, N - 1);
+        const int jlo = p.mask_kind == FA_MASKK_SLIDING ? max(qi - p.window + 1, 0) : 0;
+        const int base = k0 + 4 * half - jlo;
+        const unsigned int span = (unsigned int)(jhi - jlo);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int j = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            bool ok = j < N;
-            if (p.mask_kind != FA_MASKK_NONE) ok = ok && j <= qi;
-            if (p.mask_kind == FA_MASKK_SLIDING) ok = ok && j > qi - p.window;
-            vis |= (ok ? 1u : 0u) << (kb * 16 + r);
-            if (!ok) s[kb][r] = FA_NEG_INF;
+            const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+            s[kb][r] = (unsigned int)(base + off) <= span ? s[kb][r] : FA_NEG_INF;
           }
       }
+
+      // ---- row maximum over this block (both lane halves)
       float mx = FA_NEG_INF;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mxs = (mx == FA_NEG_INF) ? FA_NEG_INF : mx * c2;
+      const float mxs = mx * c2;
 
       // ---- raise the reference maximum when a row outgrows it
       const bool need = mxs > m_ref + FA_RESCALE_THRESHOLD;
@@ -326,6 +347,7 @@ fa_fwd_kernel(FaFwdParams p) {
         const float alpha = (m_new == m_ref) ? 1.f : exp2_hw(m_ref - m_new);
         m_ref = m_new;
         l_lane *= alpha;
+        lq_lane *= alpha;
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -333,22 +355,19 @@ fa_fwd_kernel(FaFwdParams p) {
       }
       const float m_use = (m_ref == FA_NEG_INF) ? 0.f : m_ref;
 
-      // ---- probabilities p = 2^(s*scale*log2e - m), row sum
+      // ---- probabilities p = 2^(s*scale*log2e - m)
       float pr[NKB][16];
-      float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float e = exp2_hw(__builtin_fmaf(s[kb][r], c2, -m_use));
-          if (cls == FA_TILE_PARTIAL) e = ((vis >> (kb * 16 + r)) & 1u) ? e : 0.f;
-          pr[kb][r] = e;
-          psum += e;
-        }
-      l_lane += psum;
+        for (int r = 0; r < 16; ++r) pr[kb][r] = exp2_hw(__builtin_fmaf(s[kb][r], c2, -m_use));
 
       // ---- O^T += V^T P^T
       if constexpr (G::F32) {
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) psum += pr[0][r];
+        l_lane += psum;
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -361,11 +380,26 @@ fa_fwd_kernel(FaFwdParams p) {
         // B operand (kb, t): slots 0..7 = registers 8t..8t+7, i.e. keys
         // 32kb + 16t + {4half + 0..3, 8 + 4half + 0..3}; the A operand takes
         // V^T at the same keys.
+        // Two row sums.  The output is normalised by the sum of the ROUNDED
+        // probabilities (the values the matrix core multiplies V with; two per
+        // dot2 instruction), so output and normaliser use identical weights:
+        // constant V comes out exact and a dominant key is selected exactly.
+        // lse uses the sum of the unrounded fp32 probabilities, which rounding
+        // to 16 bits would otherwise shift by up to 2^-9.
         fa_u32x4 pf[NKB][2];
+        float psum = 0.f, qsum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) pf[kb][t] = pack8<DT>(&pr[kb][8 * t]);
+          for (int t = 0; t < 2; ++t) {
+            pf[kb][t] = pack8<DT>(&pr[kb][8 * t]);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) qsum = sum2<DT>(pf[kb][t][w], qsum);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) psum += pr[kb][8 * t + i];
+          }
+        l_lane += psum;
+        lq_lane += qsum;
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -386,8 +420,10 @@ fa_fwd_kernel(FaFwdParams p) {
   }
 
   // ---- epilogue: O = O^T / l, lse = (m + log2 l) ln 2 ----------------------
+  if constexpr (G::F32) lq_lane = l_lane;  // fp32 products use p unrounded
   const float l_tot = l_lane + __shfl_xor(l_lane, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lq_tot = lq_lane + __shfl_xor(lq_lane, 32);
+  const float inv = lq_tot > 0.f ? 1.f / lq_tot : 0.f;
   const float lse = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * FA_LN2 : FA_NEG_INF;
   if (qi < N) {
     unsigned char* Ob = (unsigned char*)p.o + head_off * (OUT_F32 ? 4 : 2);
