@@ -21,6 +21,7 @@ Prints ONE JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--no-cpu-baseline] [--copy-calibration]
+       python bench.py --record-traffic FETCH_CSV WRITE_CSV WORKLOAD "COMMAND"
 """
 from __future__ import annotations
 
@@ -95,15 +96,12 @@ def load_traffic(w):
 
 def cpu_baseline(w, q, k, v, target_s: float = 12.0):
     """The oracle as it stands, timed on a bounded sample of the workload:
-    evenly spaced query rows of head (0, 0), sized for about target_s
-    seconds of CPU work; FLOPs counted as for the GPU (4*d per visible pair)."""
+    whole heads (b=0, h=0, 1, ...) while they fit in about target_s seconds
+    of CPU work, then evenly spaced rows of the next head; FLOPs counted as
+    for the GPU (4*d per visible query-key pair)."""
     import numpy as np
 
     import oracle
-
-    kk = k[0, 0].double().numpy()
-    vv = v[0, 0].double().numpy()
-    qq = q[0, 0].double().numpy()
 
     def flops_rows(rows):
         if w.mask == "none":
@@ -114,22 +112,66 @@ def cpu_baseline(w, q, k, v, target_s: float = 12.0):
             cnt = np.minimum(rows + 1, w.window)
         return 4.0 * w.d * float(cnt.sum())
 
-    def run(rows):
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def run(bh, rows):
+        b, h = heads[bh]
+        qq, kk, vv = (t[b, h].double().numpy() for t in (q, k, v))
         t0 = time.perf_counter()
         oracle.attention_rows(qq[rows], rows, kk, vv, w.scale, w.mask, w.window)
         return time.perf_counter() - t0
 
-    probe = np.linspace(0, w.N - 1, 64).astype(np.int64)
-    rate = flops_rows(probe) / max(run(probe), 1e-6)
-    per_row = flops_rows(np.arange(w.N)) / w.N
-    n_rows = int(min(w.N, max(64, target_s * rate / per_row)))
-    rows = np.linspace(0, w.N - 1, n_rows).astype(np.int64)
-    dt = run(rows)
-    fl = flops_rows(rows)
+    probe = np.linspace(0, w.N - 1, 512).astype(np.int64)
+    run(0, probe[:32])  # the first call pays thread start-up
+    rate = flops_rows(probe) / max(run(0, probe), 1e-6)
+    per_head = flops_rows(np.arange(w.N))
+    budget = target_s * rate  # FLOPs to sample
+    n_full = int(min(len(heads), budget // per_head))
+    dt, fl, n_rows = 0.0, 0.0, 0
+    for i in range(n_full):
+        allr = np.arange(w.N)
+        dt += run(i, allr)
+        fl += per_head
+        n_rows += w.N
+    if n_full < len(heads):
+        rem = int((budget - n_full * per_head) / (per_head / w.N))
+        if rem >= 16:
+            rows = np.linspace(0, w.N - 1, min(rem, w.N)).astype(np.int64)
+            dt += run(n_full, rows)
+            fl += flops_rows(rows)
+            n_rows += len(rows)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "%d evenly spaced query rows of head (b=0,h=0) of %s (%.1f GFLOP, %.1f s)"
-                      % (n_rows, w.name, fl / 1e9, dt)}
+            "sample": "%d query rows of %s: %d whole heads plus evenly spaced rows of the "
+                      "next (%.1f GFLOP, %.1f s)" % (n_rows, w.name, n_full, fl / 1e9, dt)}
+
+
+def mfma_ceiling(torch, fa, n_blocks: int = 512, iters: int = 8000):
+    """Sustained bf16 matrix-core throughput of this device (no memory
+    traffic), and the shader clock it ran at: the measured ceiling next to
+    the published peak."""
+    import numpy as np
+
+    dev = "cuda:0"
+    clk = torch.zeros(n_blocks * 4, dtype=torch.int64, device=dev)
+    sink = torch.empty(n_blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    args = (clk.data_ptr(), sink.data_ptr(), stream.cuda_stream)
+    if fa.fa_mfma_ceiling(n_blocks, 200, *args) != fa.FA_OK:
+        raise fa.FaError(fa.FA_ERR_HIP, "fa_mfma_ceiling")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    st = fa.fa_mfma_ceiling(n_blocks, iters, *args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    if st != fa.FA_OK:
+        raise fa.FaError(st, "fa_mfma_ceiling")
+    ms = e0.elapsed_time(e1)
+    c = clk.cpu().numpy().reshape(-1, 4).astype(np.float64)
+    sclk = float(np.median((c[:, 1] - c[:, 0]) / (c[:, 3] - c[:, 2]))) * 0.1  # GHz
+    flops = n_blocks * 4.0 * iters * 8 * 32768
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "sclk_ghz": round(sclk, 3),
+            "ms": round(ms, 3), "kind": "bf16 32x32x16 back-to-back, 8 chains/wave, 2 waves/SIMD"}
 
 
 def copy_calibration(torch, nbytes: int = 1 << 30):
@@ -142,7 +184,59 @@ def copy_calibration(torch, nbytes: int = 1 << 30):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
 
 
+def _pmc_rows(path):
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    per = {}
+    for r in rows:
+        key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+        per.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
+        per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+    return per
+
+
+def record_traffic(fetch_csv: str, write_csv: str, workload: str, command: str):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) of `bench.py --copy-calibration` into HBM bytes per launch of
+    the attention kernel.  Each counter is scaled by bytes / reading of the
+    plain copy of known size that the same run performs first."""
+    import seeded_inputs as si
+
+    out = {}
+    for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        per = _pmc_rows(path)
+        copies = [c[counter] for (d, k), c in sorted(per.items()) if "copyBuffer" in k]
+        attn = [c[counter] for (d, k), c in sorted(per.items()) if "fa_fwd" in k]
+        if not copies or not attn:
+            raise SystemExit("no copy or attention dispatches in %s" % path)
+        copy_kib = sorted(copies)[len(copies) // 2]
+        scale = (1 << 30) / (copy_kib * 1024.0)
+        kib = sum(attn) / len(attn)
+        out[name] = {"kib_per_launch": kib, "copy_1GiB_reads_kib": copy_kib, "scale": scale,
+                     "bytes_per_launch": kib * 1024.0 * scale, "launches": len(attn)}
+    w = si.BY_NAME[workload]
+    rec = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    if rec.get("kernel_src_sha256") != kernel_source_hash():
+        rec = {"kernel_src_sha256": kernel_source_hash(), "workloads": {}}
+    hbm = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
+    rec["workloads"][workload] = {
+        "fetch": out["fetch"], "write": out["write"], "hbm_bytes_per_launch": round(hbm),
+        "algorithmic_bytes": algorithmic_bytes(w), "ratio_to_algorithmic": hbm / algorithmic_bytes(w),
+        "command": command}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec["workloads"][workload]))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--record-traffic":
+        # --record-traffic FETCH_CSV WRITE_CSV WORKLOAD "COMMAND"
+        record_traffic(*sys.argv[2:6])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -233,6 +327,10 @@ def main():
                      "kernel_min_ms": round(min(kern_ms), 4),
                      "algorithmic_bytes": algorithmic_bytes(w)},
     }
+    if w.dtype != "f32":
+        ceil = mfma_ceiling(torch, fa)
+        res["roofline"]["measured_ceiling"] = ceil
+        res["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceil["tflops"], 4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v)
     print(json.dumps(res), flush=True)

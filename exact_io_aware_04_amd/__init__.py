@@ -3,7 +3,7 @@ gfx950 (MI355X).
 
 The functions named like the C ABI (``fa_fwd``, ``fa_fwd_record_tiles``,
 ``fa_tile_shape``, ``fa_tile_map``, ``fa_status_string``, ``fa_last_error``,
-``fa_probe_mfma``) only marshal arguments: pointers are plain integers
+``fa_probe_mfma``, ``fa_mfma_ceiling``) only marshal arguments: pointers are plain integers
 (device addresses, e.g. ``tensor.data_ptr()``), the stream is a hipStream_t
 handle (``torch.cuda.current_stream().cuda_stream``), and every step of the
 computation runs in the library's kernels.  ``attention`` is the torch-facing
@@ -64,6 +64,8 @@ def load():
     lib.fa_last_error.restype = ctypes.c_char_p
     lib.fa_probe_mfma.argtypes = [i, vp, vp, vp, vp]
     lib.fa_probe_mfma.restype = i
+    lib.fa_mfma_ceiling.argtypes = [i, i, vp, vp, vp]
+    lib.fa_mfma_ceiling.restype = i
     _lib = lib
     return lib
 
@@ -119,6 +121,10 @@ def fa_last_error() -> str:
 
 def fa_probe_mfma(which, a, b, d, stream) -> int:
     return load().fa_probe_mfma(which, a, b, d, stream)
+
+
+def fa_mfma_ceiling(n_blocks, iters, clocks, sink, stream) -> int:
+    return load().fa_mfma_ceiling(n_blocks, iters, clocks, sink, stream)
 
 
 # ---- torch convenience --------------------------------------------------------

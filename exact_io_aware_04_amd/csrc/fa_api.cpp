@@ -229,4 +229,17 @@ int fa_probe_mfma(int which, const void* a, const void* b, float* d, void* strea
   return ok();
 }
 
+int fa_mfma_ceiling(int n_blocks, int iters, unsigned long long* clocks, float* sink,
+                    void* stream) {
+  if (n_blocks < 1 || iters < 1) return fail(FA_ERR_INVALID_ARG, "n_blocks and iters must be >= 1");
+  if (!clocks || !sink) return fail(FA_ERR_INVALID_ARG, "null pointer argument");
+  if (((uintptr_t)clocks & 7u) != 0 || ((uintptr_t)sink & 3u) != 0)
+    return fail(FA_ERR_INVALID_ARG, "misaligned buffer");
+  int st = check_device();
+  if (st != FA_OK) return st;
+  hipError_t e = fa_launch_mfma_ceiling(n_blocks, iters, clocks, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "ceiling launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

@@ -585,6 +585,46 @@ __global__ void __launch_bounds__(64) fa_probe_kernel(const void* a, const void*
   for (int r = 0; r < 16; ++r) d[l * 16 + r] = c[r];
 }
 
+// Matrix-core ceiling: back-to-back independent bf16 32x32x16 products (8
+// accumulator chains per wave), no memory traffic.  Thread 0 of each
+// workgroup records the shader clock counter and the 100 MHz real-time
+// counter before and after the loop.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_mfma_ceiling_kernel(int iters, unsigned long long* clk, float* sink) {
+  const float x = 0.001f * (float)(threadIdx.x & 7);
+  fa_bf16x8 h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (__bf16)x;
+  const fa_u32x4 a = __builtin_bit_cast(fa_u32x4, h);
+  fa_f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  unsigned long long c0 = 0, r0 = 0;
+  if (threadIdx.x == 0) {
+    c0 = __builtin_readcyclecounter();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
+  for (int i = 0; i < iters; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = mma16<2>(a, a, acc[j]);
+  if (threadIdx.x == 0) {
+    const unsigned long long c1 = __builtin_readcyclecounter();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    clk[blockIdx.x * 4 + 0] = c0;
+    clk[blockIdx.x * 4 + 1] = c1;
+    clk[blockIdx.x * 4 + 2] = r0;
+    clk[blockIdx.x * 4 + 3] = r1;
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t += acc[j][r];
+  sink[blockIdx.x * 256 + threadIdx.x] = t;
+}
+
 template <int DT, int D, bool OUT_F32>
 hipError_t launch(const FaFwdParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.BH * p.n_row_tiles));
@@ -620,5 +660,11 @@ hipError_t fa_launch_probe(int which, const void* a, const void* b, float* d,
     hipLaunchKernelGGL(fa_probe_kernel<1>, dim3(1), dim3(64), 0, stream, a, b, d);
   else
     hipLaunchKernelGGL(fa_probe_kernel<2>, dim3(1), dim3(64), 0, stream, a, b, d);
+  return hipGetLastError();
+}
+
+hipError_t fa_launch_mfma_ceiling(int n_blocks, int iters, unsigned long long* clk, float* sink,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL(fa_mfma_ceiling_kernel, dim3(n_blocks), dim3(256), 0, stream, iters, clk, sink);
   return hipGetLastError();
 }

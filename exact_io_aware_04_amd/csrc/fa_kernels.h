@@ -33,3 +33,5 @@ hipError_t fa_launch_fwd(int in_dtype, int out_dtype, int d,
                          const FaFwdParams& p, hipStream_t stream);
 hipError_t fa_launch_probe(int which, const void* a, const void* b, float* d,
                            hipStream_t stream);
+hipError_t fa_launch_mfma_ceiling(int n_blocks, int iters, unsigned long long* clk, float* sink,
+                                  hipStream_t stream);

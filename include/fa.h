@@ -135,6 +135,20 @@ const char* fa_last_error(void);
 int fa_probe_mfma(int which, const void* a, const void* b, float* d,
                   void* stream);
 
+/*
+ * Diagnostic: the matrix-core ceiling of this device.  Launches n_blocks
+ * workgroups of 256 threads (two per CU fill every SIMD twice); each
+ * wavefront issues iters x 8 independent bf16 32x32x16 products (32768 FLOP
+ * each) and touches no memory in between.  clocks (device, n_blocks x 4
+ * u64): per workgroup the shader clock counter before / after the loop and
+ * the 100 MHz real-time counter before / after.  sink (device, n_blocks x
+ * 256 floats) receives the accumulators so the work is not optimised away.
+ * Sustained FLOP/s = n_blocks * 4 * iters * 8 * 32768 / elapsed time; shader
+ * clock = clock delta / real-time delta * 100 MHz.
+ */
+int fa_mfma_ceiling(int n_blocks, int iters, unsigned long long* clocks, float* sink,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

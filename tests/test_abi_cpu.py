@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = fa.load()
     names = fa.declared_functions()
     assert {"fa_fwd", "fa_fwd_record_tiles", "fa_tile_shape", "fa_tile_map",
-            "fa_status_string", "fa_last_error", "fa_probe_mfma"} <= set(names)
+            "fa_status_string", "fa_last_error", "fa_probe_mfma", "fa_mfma_ceiling"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     # and they really are C symbols of the shared object
