@@ -47,9 +47,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-int keys_per_block(int in_dtype) {
-  return in_dtype == FA_DTYPE_F32 ? FA_KEYS_32 : FA_KEYS_16;
-}
+int keys_per_block(int in_dtype, int d) { return fa_keys_per_block(in_dtype, d); }
 
 // Everything that can be decided without the device.
 int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -75,7 +73,8 @@ int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
   if (total >= 4.611686018427387904e18L)  // 2^62
     return fail(FA_ERR_INVALID_ARG, "B*H*N*d too large");
   const long long bh = (long long)B * H;
-  const long long tiles = bh * ((N + FA_ROWS_PER_WG - 1) / FA_ROWS_PER_WG);
+  const int rows_wg = fa_rows_per_wg(in_dtype, d);
+  const long long tiles = bh * ((N + rows_wg - 1) / rows_wg);
   if (tiles > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "too many row tiles for one grid");
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
   const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u;
@@ -143,7 +142,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   // is 1 to fp32 precision -- the uniform weights scale = 0 defines.
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   if (!(p.scale_log2 >= FLT_MIN)) p.scale_log2 = FLT_MIN;
-  p.n_row_tiles = (N + FA_ROWS_PER_WG - 1) / FA_ROWS_PER_WG;
+  p.n_row_tiles = (N + fa_rows_per_wg(in_dtype, d) - 1) / fa_rows_per_wg(in_dtype, d);
   p.xcd_split = (p.BH % 8 == 0) ? 1 : 0;
   p.heavy_first = mask_kind != FA_MASK_NONE ? 1 : 0;
   hipError_t e = fa_launch_fwd(in_dtype, out_dtype, d, p, (hipStream_t)stream);
@@ -176,9 +175,9 @@ int fa_tile_shape(int d, int in_dtype, int* rows_per_workgroup, int* rows_per_wa
     return fail(FA_ERR_INVALID_ARG, "null output pointer");
   if (!valid_dtype(in_dtype)) return fail(FA_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
-  *rows_per_workgroup = FA_ROWS_PER_WG;
-  *rows_per_wave = FA_ROWS_PER_WAVE;
-  *keys_per_block_out = keys_per_block(in_dtype);
+  *rows_per_workgroup = fa_rows_per_wg(in_dtype, d);
+  *rows_per_wave = FA_ROW_BLOCK;
+  *keys_per_block_out = keys_per_block(in_dtype, d);
   return ok();
 }
 
@@ -191,12 +190,12 @@ int fa_tile_map(int N, int d, int in_dtype, int mask_kind, int window, unsigned 
   if (mask_kind == FA_MASK_SLIDING && window < 1)
     return fail(FA_ERR_INVALID_ARG, "sliding window must be >= 1 (got %d)", window);
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
-  const int bc = keys_per_block(in_dtype);
-  const int R = (N + FA_ROWS_PER_WAVE - 1) / FA_ROWS_PER_WAVE;
+  const int bc = keys_per_block(in_dtype, d);
+  const int R = (N + FA_ROW_BLOCK - 1) / FA_ROW_BLOCK;
   const int C = (N + bc - 1) / bc;
   for (int rb = 0; rb < R; ++rb) {
-    const int r0 = rb * FA_ROWS_PER_WAVE;
-    const int r1 = r0 + FA_ROWS_PER_WAVE < N ? r0 + FA_ROWS_PER_WAVE : N;
+    const int r0 = rb * FA_ROW_BLOCK;
+    const int r1 = r0 + FA_ROW_BLOCK < N ? r0 + FA_ROW_BLOCK : N;
     for (int kb = 0; kb < C; ++kb)
       out[(size_t)rb * C + kb] =
           (unsigned char)fa_classify(r0, r1, kb * bc, bc, N, mask_kind, window);

@@ -65,8 +65,18 @@ typedef short fa_i16x4 __attribute__((ext_vector_type(4)));
 #define FA_RESCALE_THRESHOLD 8.0f
 // buffer descriptor word 3 for raw (unformatted, unswizzled) buffer access
 #define FA_BUF_WORD3 0x00020000
-// s_waitcnt with vmcnt(0) only (expcnt and lgkmcnt at their "no wait" maxima)
-#define FA_WAIT_VMCNT0 0x0F70
+// s_waitcnt immediate for vmcnt <= v and lgkmcnt == 0 (expcnt at its "no
+// wait" maximum; vmcnt is split over bits 3:0 and 15:14)
+#define FA_WAITCNT_VM_LGKM0(v) ((((v) & 15) | (((v) >> 4) << 14)) | (7 << 4))
+// s_waitcnt immediate for lgkmcnt == 0 only (vmcnt and expcnt at their
+// "no wait" maxima)
+#define FA_WAITCNT_LGKM0 (15 | (3 << 14) | (7 << 4))
+
+// Workgroup barrier without a memory fence: the caller has already waited
+// for exactly the memory operations that must be complete.  (A fenced
+// barrier would also wait for the K/V blocks still in flight.)  The asm is a
+// compiler memory barrier, so no LDS access moves across it.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 
 namespace {
 
@@ -143,6 +153,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 // ---------------------------------------------------------------------------
 
 // Work item of this workgroup: (batch*head, first query row).
+template <int ROWS_WG>
 __device__ __forceinline__ void work_item(const FaFwdParams& p, int& bh, int& q0) {
   const int T = p.n_row_tiles;
   const int b = blockIdx.x;
@@ -157,7 +168,7 @@ __device__ __forceinline__ void work_item(const FaFwdParams& p, int& bh, int& q0
     rank = b / p.BH;
   }
   const int qt = p.heavy_first ? (T - 1 - rank) : rank;
-  q0 = qt * FA_ROWS_PER_WG;
+  q0 = qt * ROWS_WG;
 }
 
 // Boundary blocks: scores of invisible keys become -inf, which the
@@ -212,15 +223,13 @@ __device__ __forceinline__ void softmax_block(fa_f32x16 (&s)[NKB], float (&pr)[N
     for (int r = 0; r < 16; ++r) pr[kb][r] = exp2_hw(__builtin_fmaf(s[kb][r], c2, -m_use));
 }
 
-// O = O^T / l (sum of the probabilities used in the product with V),
-// lse = (m + log2 l) ln 2 (sum of the unrounded probabilities).
+// O = O^T / lq (row sum of the probabilities used in the product with V),
+// lse = (m + log2 l) ln 2 (l: row sum of the unrounded probabilities).
 template <int DT, int D, bool OUT_F32>
 __device__ __forceinline__ void store_output(const FaFwdParams& p, const fa_f32x16 (&acc)[D / 32],
-                                             float m_ref, float l_lane, float lq_lane, int bh,
+                                             float m_ref, float l_tot, float lq_tot, int bh,
                                              int qi, int half) {
   const int N = p.N;
-  const float l_tot = pair_sum(l_lane);
-  const float lq_tot = pair_sum(lq_lane);
   const float inv = lq_tot > 0.f ? 1.f / lq_tot : 0.f;
   const float lse = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * FA_LN2 : FA_NEG_INF;
   if (qi >= N) return;
@@ -247,46 +256,135 @@ __device__ __forceinline__ void store_output(const FaFwdParams& p, const fa_f32x
 // bf16 / f16 kernel
 // ---------------------------------------------------------------------------
 
-// 16-byte chunk swizzles (row r): K rows are read 16 rows x one chunk per
-// 16 lanes, V rows 8 rows x 4 chunks per wavefront by the transposing read.
+// 16-byte chunk swizzles (chunk position = chunk ^ swizzle of the row).  K
+// rows are read 16 rows x one chunk per 16 lanes, V rows 8 rows x 4 chunks
+// per wavefront by the transposing read; each swizzle spreads every such
+// access over distinct chunk slots of the LDS banks.
 template <int D>
-__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1)); }
 template <int D>
 __device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
+// Matrix phase of one wavefront: S^T = K Q^T over the current key block (QK)
+// and O^T += V^T P^T over the previous one (PV), as one software-pipelined
+// sequence of products whose LDS operands are read FA_OPND_AHEAD products
+// ahead.  The wavefront issues its products while its SIMD partner computes
+// a softmax, so nothing else hides the LDS latency.  The scores come first:
+// the softmax that follows waits only for them, while the P V products are
+// still executing.  Product order: Q K by contraction slice s, then key
+// group kb (the score accumulators starting from sc0); then P V by (kb,
+// half t), then output block cb, so consecutive products update different
+// accumulators; last, four products of an all-ones operand with the P^T
+// operands add the block's rounded probabilities to the row sums lsum.  The
+// K operand of (s, kb) is one 16-byte read of row
+// 32kb + l32, chunk 2s + half; the V^T operand of (kb, t, cb) two
+// transposing reads at rows 32kb + 16t + 4half + 0..3 and + 8 (the keys of
+// the P^T operand).
+#define FA_OPND_AHEAD 6
+template <int DT, int D, bool PV, bool QK>
+__device__ __forceinline__ void matrix_phase(fa_f32x16 (&acc)[D / 32], fa_f32x16 (&sc)[2],
+                                             fa_f32x16& lsum, const fa_f32x16& sc0,
+                                             const fa_u32x4 (&pf)[2][2], const fa_u32x4 (&qf)[D / 16],
+                                             const FA_AS3 unsigned char* kcur,
+                                             const FA_AS3 unsigned char* vcur,
+                                             const unsigned (&kread)[D / 16],
+                                             const unsigned (&vread)[D / 32]) {
+  constexpr int NCB = D / 32, NQF = D / 16, ROWB = 2 * D;
+  constexpr int NQK = QK ? 2 * NQF : 0;
+  constexpr int NOPS = NQK + (PV ? 4 * NCB : 0);
+  constexpr int R = FA_OPND_AHEAD;
+  constexpr int NSLOT = R + 1;  // the slot being filled is never the one being read
+  fa_u32x4 opnd[NSLOT];
+  if constexpr (QK) {
+    sc[0] = sc0;
+    sc[1] = sc0;
+  }
+#pragma unroll
+  for (int i = 0; i < NOPS + R; ++i) {
+    if (i >= R) {  // product i - R
+      const int j = i - R;
+      if (j < NQK) {
+        const int sl = j / 2, kb = j % 2;
+        sc[kb] = mma16<DT>(opnd[j % NSLOT], qf[sl], sc[kb]);
+      } else {
+        const int q = j - NQK, cb = q % NCB, kb = q / NCB / 2, t = q / NCB % 2;
+        acc[cb] = mma16<DT>(opnd[j % NSLOT], pf[kb][t], acc[cb]);
+      }
+    }
+    if (i < NOPS) {  // operand of product i
+      if (i < NQK) {
+        const int sl = i / 2, kb = i % 2;
+        opnd[i % NSLOT] = *(const FA_AS3 fa_u32x4*)(kcur + kb * 32 * ROWB + kread[sl]);
+      } else {
+        const int q = i - NQK, cb = q % NCB, kb = q / NCB / 2, t = q / NCB % 2;
+        const FA_AS3 unsigned char* vp = vcur + (32 * kb + 16 * t) * ROWB + vread[cb];
+        const fa_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_AS3 fa_i16x4*)vp);
+        const fa_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_AS3 fa_i16x4*)(vp + 8 * ROWB));
+        const fa_u32x2 l2 = __builtin_bit_cast(fa_u32x2, lo), h2 = __builtin_bit_cast(fa_u32x2, hi);
+        opnd[i % NSLOT] = fa_u32x4{l2.x, l2.y, h2.x, h2.y};
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (PV) {
+    // row sums of the rounded probabilities: an all-ones A operand times the
+    // same P^T operands (every lane then holds its row's sum in every register)
+    constexpr unsigned ONE2 = DT == 2 ? 0x3F803F80u : 0x3C003C00u;
+    const fa_u32x4 ones = {ONE2, ONE2, ONE2, ONE2};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) lsum = mma16<DT>(ones, pf[kb][t], lsum);
+  }
+}
+
+// Eight wavefronts, 32 query rows each, two per SIMD.  The two wavefronts of
+// a SIMD run half a key block apart ("ping-pong"): while one issues the
+// matrix products of a block, the other computes the softmax of its block,
+// so the matrix cores and the vector ALUs work at the same time.  Wavefronts
+// 0-3 lead, 4-7 trail; a workgroup barrier between half steps keeps the two
+// groups in opposite phases.
 template <int DT, int D, bool OUT_F32>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(FA_WAVES_16 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd16_kernel(FaFwdParams p) {
+  constexpr int NW = FA_WAVES_16;
+  constexpr int ROWS_WG = NW * FA_ROW_BLOCK;
   constexpr int BC = FA_KEYS_16;   // keys per block
   constexpr int NKB = BC / 32;     // 32-key groups per block
   constexpr int NCB = D / 32;      // 32-column output blocks
   constexpr int NQF = D / 16;      // 16-deep slices of the QK^T contraction
   constexpr int ROWB = 2 * D;      // bytes of one K/V row
   constexpr int TILEB = BC * ROWB; // bytes of one K or V block
-  constexpr int LPW = TILEB / (FA_WAVES * 1024);  // 1 KB loads per wave per matrix
-  static_assert(LPW * FA_WAVES * 1024 == TILEB, "loads must cover the block");
-  // LDS: K and V, double-buffered, as four separate objects so that the
-  // compiler can tell the block being read from the one being filled (and
-  // does not wait for the prefetch before reading the current block)
-  __shared__ __attribute__((aligned(1024))) unsigned char ks0[TILEB], ks1[TILEB], vs0[TILEB], vs1[TILEB];
-  // (the lambdas below take the buffer index as a plain int: every call
-  // passes a constant, so the selections fold away after inlining)
-  auto kbuf = [&](int b) { return (FA_AS3 unsigned char*)(b ? ks1 : ks0); };
-  auto vbuf = [&](int b) { return (FA_AS3 unsigned char*)(b ? vs1 : vs0); };
+  constexpr int NL = NW / 2;       // wavefronts that load K and V (the leading ones)
+  constexpr int LPW = TILEB / (NL * 1024);  // 1 KB loads per loading wave per matrix
+  static_assert(LPW * NL * 1024 == TILEB, "loads must cover the block");
+  static_assert(NL * 1024 / ROWB % 16 == 0, "pieces must be a multiple of 16 rows apart");
+  static_assert(NW == 8 && FA_STAGES_16 == 3, "schedule below: 2 x 4 wavefronts, rings of 3");
+  // LDS: rings of three K and three V blocks, as separate objects so that
+  // the compiler can tell the slots being read from the ones being filled
+  // (and does not wait for the prefetches before reading)
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[TILEB], ks1[TILEB], ks2[TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs0[TILEB], vs1[TILEB], vs2[TILEB];
+  // (the lambdas below take the slot index as a plain int: every call passes
+  // a constant, so the selections fold away after inlining)
+  auto kbuf = [&](int b) { return (FA_AS3 unsigned char*)(b == 0 ? ks0 : b == 1 ? ks1 : ks2); };
+  auto vbuf = [&](int b) { return (FA_AS3 unsigned char*)(b == 0 ? vs0 : b == 1 ? vs1 : vs2); };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool lead = wave < NW / 2;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int half = lane >> 5;
   const int N = p.N;
 
   int bh, q0;
-  work_item(p, bh, q0);
-  const int q1 = min(q0 + FA_ROWS_PER_WG, N);
-  const int qw0 = q0 + wave * FA_ROWS_PER_WAVE;
-  const int qw1 = min(qw0 + FA_ROWS_PER_WAVE, N);
-  const int qi = qw0 + l32;  // this lane's query row
+  work_item<ROWS_WG>(p, bh, q0);
+  const int q1 = min(q0 + ROWS_WG, N);
+  // this wave's rows qb0 .. qb1-1; this lane's row qi
+  const int qb0 = q0 + wave * FA_ROW_BLOCK;
+  const int qb1 = min(qb0 + FA_ROW_BLOCK, N);
+  const int qi = qb0 + l32;
 
   const size_t head_bytes = (size_t)N * ROWB;
   const unsigned char* Qh = (const unsigned char*)p.q + (size_t)bh * head_bytes;
@@ -305,15 +403,16 @@ fa_fwd16_kernel(FaFwdParams p) {
     for (int ks = 0; ks < NQF; ++ks) qf[ks] = *(const fa_u32x4*)(qrow + ks * 32 + half * 16);
   }
 
-  // Global byte offsets (within a block) of this lane's 16 bytes in each of
-  // the wave's LPW one-kilobyte LDS pieces, swizzle applied.
-  unsigned koff[LPW], voff[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int o = (i * FA_WAVES + wave) * 1024 + 16 * lane;
+  // Global byte offset (within a block) of this lane's 16 bytes in a loading
+  // wave's first one-kilobyte LDS piece, swizzle applied.  Piece i lies 4 KB
+  // (16 or 32 rows) further on both sides: the swizzles depend on row bits
+  // that a multiple of 16 rows leaves unchanged.
+  unsigned koff, voff;
+  {
+    const int o = (wave % NL) * 1024 + 16 * lane;
     const int r = o / ROWB, pos = (o % ROWB) / 16;
-    koff[i] = r * ROWB + 16 * (pos ^ kswz<D>(r));
-    voff[i] = r * ROWB + 16 * (pos ^ vswz<D>(r));
+    koff = r * ROWB + 16 * (pos ^ kswz<D>(r));
+    voff = r * ROWB + 16 * (pos ^ vswz<D>(r));
   }
   // LDS read offsets: K slice s of row l32 (chunk 2s + half); V^T pieces for
   // output block cb (row 4half + t, columns 32cb + 16(lane/16 mod 2) + 4q).
@@ -327,134 +426,227 @@ fa_fwd16_kernel(FaFwdParams p) {
       vread[cb] = (4 * half + t) * ROWB + 64 * (cb ^ (D == 128 ? t : (t >> 1))) + 32 * (g & 1) + 8 * q;
   }
 
-  // Block kt -> LDS buffer buf.  The descriptor's base is the block's first
+  // K or V block kt -> LDS slot.  The descriptor's base is the block's first
   // key and its size stops at key N, so rows past N read as zeros.  (The
   // offsets are passed as int prvalues: handing the builtin the captured
   // array element itself keeps hipcc's host pass from emitting the kernel's
   // launch stub.)
-  auto issue = [&](int kt, int buf) {
-    FA_AS3 unsigned char* const kdst = kbuf(buf);
-    FA_AS3 unsigned char* const vdst = vbuf(buf);
+  auto issue = [&](const unsigned char* base, unsigned off, FA_AS3 unsigned char* dst, int kt) {
     const int k0 = kt * BC;
     const int nb = (min(N - k0, BC)) * ROWB;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Kh + (size_t)k0 * ROWB), 0, nb, FA_BUF_WORD3);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Vh + (size_t)k0 * ROWB), 0, nb, FA_BUF_WORD3);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * ROWB), 0, nb, FA_BUF_WORD3);
 #pragma unroll
     for (int i = 0; i < LPW; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (FA_AS3 void*)(kdst + (i * FA_WAVES + wave) * 1024), 16, (int)koff[i], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < LPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (FA_AS3 void*)(vdst + (i * FA_WAVES + wave) * 1024), 16, (int)voff[i], 0, 0, 0);
+          rsrc, (FA_AS3 void*)(dst + (i * NL + wave) * 1024), 16, (int)off, i * NL * 1024, 0, 0);
   };
 
-  fa_f32x16 acc[NCB];  // O^T: block cb holds columns 32cb.., row qi
+  fa_f32x16 acc[NCB];  // O^T: acc[cb] holds columns 32cb.., row qi
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-  float m_ref = FA_NEG_INF;  // reference maximum (base-2 scaled units)
-  float l_lane = 0.f;        // this lane's part of the exponent sum
-  float lq_lane = 0.f;       // same, of the probabilities as rounded for P V
+  // reference (base 2) and this lane's sum of unrounded probabilities; the
+  // row sums of the rounded ones accumulate on the matrix core, in lsum
+  float m_ref = FA_NEG_INF, l_lane = 0.f;
+  fa_f32x16 lsum;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lsum[r] = 0.f;
   const float c2 = p.scale_log2;
-  const int n_row_blocks = (N + FA_ROWS_PER_WAVE - 1) / FA_ROWS_PER_WAVE;
+  const int n_row_blocks = (N + FA_ROW_BLOCK - 1) / FA_ROW_BLOCK;
   const int n_key_blocks = (N + BC - 1) / BC;
-  const int row_block = qw0 / FA_ROWS_PER_WAVE;
 
-  // One key block: prefetch the next into the other buffer, compute this one
-  // (unless fully masked for this wave), wait for the prefetch, barrier.
-  auto body = [&](int kt, int buf) {
-    FA_AS3 unsigned char* const kcur = kbuf(buf);
-    FA_AS3 unsigned char* const vcur = vbuf(buf);
-    if (kt + 1 < kv_hi) issue(kt + 1, 1 - buf);
-    const int k0 = kt * BC;
-    const int cls = fa_classify(qw0, qw1, k0, BC, N, p.mask_kind, p.window);
-    if (p.tiles && lane == 0 && qw0 < N)
-      p.tiles[((size_t)bh * n_row_blocks + row_block) * n_key_blocks + kt] = (unsigned char)(cls + 1);
-    if (cls != FA_TILE_SKIP) {
-      // S^T = K Q^T: s[kb][r] is key k0 + 32kb + 8(r/4) + 4half + r%4
-      fa_f32x16 s[NKB];
+  // Carried between the phases: scores of the current block (matrix phase
+  // -> softmax phase) and its rounded probabilities (softmax phase -> the
+  // next matrix phase).  s[kb][r] is key k0 + 32kb + 8(r/4) + 4half + r%4 of
+  // row qi; P^T operand (kb, t) holds registers 8t..8t+7 of s[kb], i.e. keys
+  // 32kb + 16t + {4half + 0..3, 8 + 4half + 0..3}.
+  fa_f32x16 sc[NKB];
+  fa_u32x4 pf[NKB][2];
+  // Start value of the score accumulators: -m_use / c2 in all 16 registers
+  // (m_use = m_ref, or 0 while the row has seen no key), so that the matrix
+  // core delivers t / c2 with t = s c2 - m_use, the exponent of the
+  // probability, and the softmax needs one multiply per score instead of an
+  // FMA with the per-row reference (one VGPR operand instead of two: beside
+  // the partner wave's matrix products every VALU instruction with two or
+  // more VGPR operands costs one extra issue cycle of four).
+  fa_f32x16 sc0;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+  for (int r = 0; r < 16; ++r) sc0[r] = 0.f;
+  const float inv_c2 = 1.f / p.scale_log2;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < NQF; ++ks) {
-          const fa_u32x4 a = *(const FA_AS3 fa_u32x4*)(kcur + kb * 32 * ROWB + kread[ks]);
-          s[kb] = mma16<DT>(a, qf[ks], s[kb]);
-        }
-      }
-      if (cls == FA_TILE_PARTIAL) apply_mask<NKB>(s, k0, qi, half, N, p.mask_kind, p.window);
-      float pr[NKB][16];
-      softmax_block<NKB, NCB>(s, pr, acc, m_ref, l_lane, lq_lane, c2);
+    for (int t = 0; t < 2; ++t) pf[kb][t] = fa_u32x4{0u, 0u, 0u, 0u};
 
-      // Two row sums.  The output is normalised by the sum of the ROUNDED
-      // probabilities (the values the matrix core multiplies V with; two per
-      // dot2), so output and normaliser use identical weights: constant V
-      // comes out exact and a dominant key is selected exactly.  lse uses the
-      // sum of the unrounded probabilities, which rounding to 16 bits would
-      // otherwise move by up to 2^-9.
-      // B operand (kb, t): slots 0..7 = registers 8t..8t+7, i.e. keys
-      // 32kb + 16t + {4half + 0..3, 8 + 4half + 0..3}.
-      fa_u32x4 pf[NKB][2];
-      float psum = 0.f, qsum = 0.f;
+  // Matrix phase of step kt: O^T += V^T P^T for block kt-1 (V slot vs) and
+  // S^T = K Q^T for block kt (K slot ks).  It runs in full even where the
+  // row block sees no key of one of the blocks (the workgroup's barriers
+  // pace every wave anyway, and one code path keeps the registers in
+  // place): the probabilities of a skipped block are 0, which adds exactly
+  // 0 to O, and the scores of a skipped block are never used.
+  auto phase_mfma = [&](int ks, int vs) {
+    matrix_phase<DT, D, true, true>(acc, sc, lsum, sc0, pf, qf, kbuf(ks), vbuf(vs), kread, vread);
+  };
+  // Softmax phase of block kt (classification cls).
+  // Softmax phase of block kt (classification cls).  Fast path (fully
+  // visible block, row already started): p = 2^t straight from the scores;
+  // the row sums show whether any p exceeds 2^8 (a score more than 8 base-2
+  // units above the reference; the same laziness as the max test of the
+  // exact path).  Exact path (boundary block, a row's first block, or a
+  // lane's sum above 2^8, infinite or NaN): mask, row maximum, new reference
+  // at the exact maximum, rescale of O and the sums, probabilities again.
+  auto phase_softmax = [&](int kt, int cls) {
+    if (cls == FA_TILE_SKIP) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          pf[kb][t] = pack8<DT>(&pr[kb][8 * t]);
+        for (int t = 0; t < 2; ++t) pf[kb][t] = fa_u32x4{0u, 0u, 0u, 0u};
+      return;
+    }
+    float pr[NKB][16];
+    float psum = 0.f;
+    bool exact = cls == FA_TILE_PARTIAL || __ballot(m_ref == FA_NEG_INF);
+    if (!exact) {
 #pragma unroll
-          for (int w = 0; w < 4; ++w) qsum = sum2<DT>(pf[kb][t][w], qsum);
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) psum += pr[kb][8 * t + i];
+        for (int r = 0; r < 16; ++r) {
+          pr[kb][r] = exp2_hw(sc[kb][r] * c2);
+          psum += pr[kb][r];
         }
-      l_lane += psum;
-      lq_lane += qsum;
-
-      // O^T += V^T P^T; the A operand holds V at the same keys: rows
-      // 32kb + 16t + 4half + 0..3 (first read) and + 8 (second read).
+      exact = __ballot(!(psum <= 256.f));
+    }
+    if (exact) {
+      if (cls == FA_TILE_PARTIAL) apply_mask<NKB>(sc, kt * BC, qi, half, N, p.mask_kind, p.window);
+      const float m_use = m_ref == FA_NEG_INF ? 0.f : m_ref;
+      float mx = FA_NEG_INF;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx = pair_max(mx) * c2;  // block maximum of t (-inf: nothing visible)
+      const float m_new = fmaxf(m_ref, mx == FA_NEG_INF ? FA_NEG_INF : m_use + mx);
+      const float alpha = m_new > m_ref ? (m_ref == FA_NEG_INF ? 0.f : exp2_hw(m_ref - m_new)) : 1.f;
+      m_ref = m_new;
+      l_lane *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lsum[r] *= alpha;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+      const float shift = m_ref == FA_NEG_INF ? 0.f : m_use - m_ref;
+      psum = 0.f;
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            FA_AS3 unsigned char* vp = vcur + (32 * kb + 16 * t) * ROWB + vread[cb];
-            const fa_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_AS3 fa_i16x4*)vp);
-            const fa_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_AS3 fa_i16x4*)(vp + 8 * ROWB));
-            const fa_u32x2 l2 = __builtin_bit_cast(fa_u32x2, lo), h2 = __builtin_bit_cast(fa_u32x2, hi);
-            const fa_u32x4 a = {l2.x, l2.y, h2.x, h2.y};
-            acc[cb] = mma16<DT>(a, pf[kb][t], acc[cb]);
-          }
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          pr[kb][r] = exp2_hw(__builtin_fmaf(sc[kb][r], c2, shift));
+          psum += pr[kb][r];
+        }
+      const float mn = m_ref == FA_NEG_INF ? 0.f : -m_ref * inv_c2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc0[r] = mn;
     }
-    __builtin_amdgcn_s_waitcnt(FA_WAIT_VMCNT0);
-    __syncthreads();
+    // Two row sums.  The output is normalised by the sum of the ROUNDED
+    // probabilities (the values the matrix core multiplies V with; summed on
+    // the matrix core in the next matrix phase), so output and normaliser
+    // use identical weights: constant V comes out exact and a dominant key
+    // is selected exactly.  lse uses the sum of the unrounded probabilities,
+    // which rounding to 16 bits would otherwise move by up to 2^-9.
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) pf[kb][t] = pack8<DT>(&pr[kb][8 * t]);
+    l_lane += psum;
+  };
+
+  // Loads of step kt (leading waves only): K(kt+2) and V(kt+1) into the
+  // slots freed by K(kt-1) and V(kt-2) (K slot of block kt:
+  // (kt - kv_lo) mod 3 = s).  The matching wait lets exactly these stay in
+  // flight, so K(kt+1) and V(kt) have landed (loads complete in issue order).
+  auto issue_step = [&](int kt, int s) {
+    if (kt + 2 < kv_hi) issue(Kh, koff, kbuf((s + 2) % 3), kt + 2);
+    if (kt + 1 < kv_hi) issue(Vh, voff, vbuf((s + 1) % 3), kt + 1);
+  };
+  auto wait_step = [&](int kt) {
+    const int n_new = (kt + 2 < kv_hi) + (kt + 1 < kv_hi);
+    if (n_new == 2)
+      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(2 * LPW));
+    else if (n_new == 1)
+      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(LPW));
+    else
+      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
+  };
+
+  // Every wave runs, for kt = kv_lo .. kv_hi: matrix phase kt (P V of block
+  // kt-1 and the scores of block kt), barrier, softmax phase kt, barrier.
+  // The trailing waves pass one barrier before their first step, the leading
+  // ones one after their last, so a trailing wave's matrix phase kt runs
+  // beside the leading waves' softmax phase kt, and its softmax phase kt
+  // beside their matrix phase kt+1.  In half steps h (the intervals between
+  // consecutive barriers; h = 2(kt - kv_lo) is the leading waves' matrix
+  // phase kt): step kt's loads start at the beginning of h and are waited
+  // for at the end of h + 1, before the barrier.  Matrix phase kt reads
+  // K(kt) and V(kt-1) in h and h + 1; those slots are refilled at h + 2 at
+  // the earliest, after every wave has finished its LDS reads (lgkmcnt(0)
+  // before each barrier); the wait at the end of h + 1 makes K(kt+1) and
+  // V(kt), needed from h + 2 on, visible to every wave.
+  int cls_prev = FA_TILE_SKIP;
+  auto step = [&](int kt, int s) {
+    int cls_cur = FA_TILE_SKIP;
+    if (kt < kv_hi) {
+      cls_cur = fa_classify(qb0, qb1, kt * BC, BC, N, p.mask_kind, p.window);
+      if (p.tiles && lane == 0 && qb0 < N)
+        p.tiles[((size_t)bh * n_row_blocks + qb0 / FA_ROW_BLOCK) * n_key_blocks + kt] =
+            (unsigned char)(cls_cur + 1);
+    }
+    if (lead) issue_step(kt, s);
+    phase_mfma(s, (s + 2) % 3);
+    __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
+    barrier_nofence();
+    phase_softmax(kt, cls_cur);
+    if (lead) wait_step(kt);
+    __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
+    barrier_nofence();
+    cls_prev = cls_cur;
   };
 
   // Every workgroup has at least one key block: row q0 < N always sees key
-  // q0 itself (the diagonal is visible under every mask).
-  issue(kv_lo, 0);
-  // Q fragments and the first block have landed before the loop starts, so
-  // the loop's prefetch never waits behind them.
+  // q0 itself (the diagonal is visible under every mask).  Prologue: K of
+  // the first two blocks, V of the first, and zeros in the V slot that the
+  // first step's (probability 0) P V product reads.
+  if (lead) {
+    issue(Kh, koff, kbuf(0), kv_lo);
+    if (kv_lo + 1 < kv_hi) issue(Kh, koff, kbuf(1), kv_lo + 1);
+    issue(Vh, voff, vbuf(0), kv_lo);
+  }
+#pragma unroll
+  for (int i = 0; i < TILEB / (NW * 64 * 16); ++i)
+    *(FA_AS3 fa_u32x4*)(vbuf(2) + (i * NW * 64 + tid) * 16) = fa_u32x4{0u, 0u, 0u, 0u};
+  static_assert(TILEB % (NW * 64 * 16) == 0, "zero fill must cover the slot");
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (!lead) barrier_nofence();
   for (int kt = kv_lo;;) {
-    body(kt, 0);
-    if (++kt >= kv_hi) break;
-    body(kt, 1);
-    if (++kt >= kv_hi) break;
+    step(kt, 0);
+    if (++kt > kv_hi) break;
+    step(kt, 1);
+    if (++kt > kv_hi) break;
+    step(kt, 2);
+    if (++kt > kv_hi) break;
   }
-  store_output<DT, D, OUT_F32>(p, acc, m_ref, l_lane, lq_lane, bh, qi, half);
+  if (lead) barrier_nofence();
+  store_output<DT, D, OUT_F32>(p, acc, m_ref, pair_sum(l_lane), lsum[0], bh, qi, half);
 }
 
 // ---------------------------------------------------------------------------
 // fp32 kernel (v_mfma_f32_32x32x2f32; one contraction element per lane)
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(FA_WAVES_32 * 64)
 __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2)))
 fa_fwd32_kernel(FaFwdParams p) {
   constexpr int BC = FA_KEYS_32;       // keys per block (one 32-key group)
@@ -474,10 +666,10 @@ fa_fwd32_kernel(FaFwdParams p) {
   const int N = p.N;
 
   int bh, q0;
-  work_item(p, bh, q0);
-  const int q1 = min(q0 + FA_ROWS_PER_WG, N);
-  const int qw0 = q0 + wave * FA_ROWS_PER_WAVE;
-  const int qw1 = min(qw0 + FA_ROWS_PER_WAVE, N);
+  work_item<FA_WAVES_32 * FA_ROW_BLOCK>(p, bh, q0);
+  const int q1 = min(q0 + FA_WAVES_32 * FA_ROW_BLOCK, N);
+  const int qw0 = q0 + wave * FA_ROW_BLOCK;
+  const int qw1 = min(qw0 + FA_ROW_BLOCK, N);
   const int qi = qw0 + l32;
   const size_t head = (size_t)bh * N * D;
   const float* Qh = (const float*)p.q + head;
@@ -521,9 +713,9 @@ fa_fwd32_kernel(FaFwdParams p) {
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
   float m_ref = FA_NEG_INF, l_lane = 0.f, lq_lane = 0.f;
   const float c2 = p.scale_log2;
-  const int n_row_blocks = (N + FA_ROWS_PER_WAVE - 1) / FA_ROWS_PER_WAVE;
+  const int n_row_blocks = (N + FA_ROW_BLOCK - 1) / FA_ROW_BLOCK;
   const int n_key_blocks = (N + BC - 1) / BC;
-  const int row_block = qw0 / FA_ROWS_PER_WAVE;
+  const int row_block = qw0 / FA_ROW_BLOCK;
 
   gload(kv_lo);
   lstore(0);
@@ -563,7 +755,7 @@ fa_fwd32_kernel(FaFwdParams p) {
     if (has_next) lstore(buf ^ 1);
     __syncthreads();
   }
-  store_output<0, D, true>(p, acc, m_ref, l_lane, lq_lane, bh, qi, half);
+  store_output<0, D, true>(p, acc, m_ref, pair_sum(l_lane), pair_sum(lq_lane), bh, qi, half);
 }
 
 // One wavefront, one product: lane-order operands in, lane-order accumulator
@@ -629,9 +821,9 @@ template <int DT, int D, bool OUT_F32>
 hipError_t launch(const FaFwdParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.BH * p.n_row_tiles));
   if constexpr (DT == 0)
-    hipLaunchKernelGGL((fa_fwd32_kernel<D>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fa_fwd32_kernel<D>), grid, dim3(FA_WAVES_32 * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((fa_fwd16_kernel<DT, D, OUT_F32>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fa_fwd16_kernel<DT, D, OUT_F32>), grid, dim3(FA_WAVES_16 * 64), 0, stream, p);
   return hipGetLastError();
 }
 

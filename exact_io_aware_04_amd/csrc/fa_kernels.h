@@ -21,12 +21,24 @@ struct FaFwdParams {
   int heavy_first;        // 1: longest row tiles launched first (masks)
 };
 
-// Tile geometry per input precision.
-constexpr int FA_WAVES = 4;              // wavefronts per workgroup
-constexpr int FA_ROWS_PER_WAVE = 32;     // query rows owned by one wavefront
-constexpr int FA_ROWS_PER_WG = FA_WAVES * FA_ROWS_PER_WAVE;
+// Tile geometry.  Work is skipped per row block of 32 query rows (one
+// 32x32 matrix-core tile of rows); each wavefront owns one row block.
+constexpr int FA_ROW_BLOCK = 32;         // query rows per row block
+constexpr int FA_WAVES_32 = 4;           // wavefronts per workgroup, f32
+constexpr int FA_WAVES_16 = 8;           // wavefronts per workgroup, f16/bf16
 constexpr int FA_KEYS_16 = 64;           // keys per K/V block, f16/bf16
 constexpr int FA_KEYS_32 = 32;           // keys per K/V block, f32
+constexpr int FA_STAGES_16 = 3;          // depth of the K and V rings in LDS, f16/bf16
+
+// keys per K/V block for an input dtype code (0 = f32) and head dim
+constexpr int fa_keys_per_block(int in_dtype, int d) {
+  return in_dtype == 0 ? FA_KEYS_32 : FA_KEYS_16;
+}
+
+// query rows per workgroup for an input dtype code (0 = f32) and head dim
+constexpr int fa_rows_per_wg(int in_dtype, int d) {
+  return (in_dtype == 0 ? FA_WAVES_32 : FA_WAVES_16) * FA_ROW_BLOCK;
+}
 
 // dtype codes as in fa.h
 hipError_t fa_launch_fwd(int in_dtype, int out_dtype, int d,

@@ -103,8 +103,8 @@ def test_probe_rejects_bad_arguments():
 
 
 def test_tile_shape():
-    assert fa.fa_tile_shape(128, fa.FA_DTYPE_BF16) == (128, 32, 64)
-    assert fa.fa_tile_shape(64, fa.FA_DTYPE_F16) == (128, 32, 64)
+    assert fa.fa_tile_shape(128, fa.FA_DTYPE_BF16) == (256, 32, 64)
+    assert fa.fa_tile_shape(64, fa.FA_DTYPE_F16) == (256, 32, 64)
     assert fa.fa_tile_shape(64, fa.FA_DTYPE_F32) == (128, 32, 32)
 
 
