@@ -355,8 +355,8 @@ fa_fwd16_kernel(FaFwdParams p) {
   constexpr int NQF = D / 16;      // 16-deep slices of the QK^T contraction
   constexpr int ROWB = 2 * D;      // bytes of one K/V row
   constexpr int TILEB = BC * ROWB; // bytes of one K or V block
-  constexpr int NL = NW / 2;       // wavefronts that load K and V (the leading ones)
-  constexpr int LPW = TILEB / (NL * 1024);  // 1 KB loads per loading wave per matrix
+  constexpr int NL = NW / 2;       // wavefronts loading each matrix (K: leading, V: trailing)
+  constexpr int LPW = TILEB / (NL * 1024);  // 1 KB loads per loading wave per block
   static_assert(LPW * NL * 1024 == TILEB, "loads must cover the block");
   static_assert(NL * 1024 / ROWB % 16 == 0, "pieces must be a multiple of 16 rows apart");
   static_assert(NW == 8 && FA_STAGES_16 == 3, "schedule below: 2 x 4 wavefronts, rings of 3");
@@ -439,7 +439,7 @@ fa_fwd16_kernel(FaFwdParams p) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (FA_AS3 void*)(dst + (i * NL + wave) * 1024), 16, (int)off, i * NL * 1024, 0, 0);
+          rsrc, (FA_AS3 void*)(dst + (i * NL + wave % NL) * 1024), 16, (int)off, i * NL * 1024, 0, 0);
   };
 
   fa_f32x16 acc[NCB];  // O^T: acc[cb] holds columns 32cb.., row qi
@@ -563,37 +563,42 @@ fa_fwd16_kernel(FaFwdParams p) {
     l_lane += psum;
   };
 
-  // Loads of step kt (leading waves only): K(kt+2) and V(kt+1) into the
-  // slots freed by K(kt-1) and V(kt-2) (K slot of block kt:
-  // (kt - kv_lo) mod 3 = s).  The matching wait lets exactly these stay in
-  // flight, so K(kt+1) and V(kt) have landed (loads complete in issue order).
+  // Loads.  K(j) and V(j) live in ring slot (j - kv_lo) mod 3.  At the end
+  // of its softmax phase kt (where it would otherwise wait at the barrier) a
+  // leading wave issues its share of K(kt+2), a trailing wave its share of
+  // V(kt+2), into the slots of block kt-1, whose last reader (matrix phase
+  // kt-1 for K, matrix phase kt for V) has passed a barrier since.  The wait
+  // that follows lets these stay in flight, so the wave's loads of the
+  // previous step, K(kt+1) or V(kt+1), have landed (loads complete in issue
+  // order).
   auto issue_step = [&](int kt, int s) {
-    if (kt + 2 < kv_hi) issue(Kh, koff, kbuf((s + 2) % 3), kt + 2);
-    if (kt + 1 < kv_hi) issue(Vh, voff, vbuf((s + 1) % 3), kt + 1);
+    if (kt + 2 < kv_hi) {
+      if (lead)
+        issue(Kh, koff, kbuf((s + 2) % 3), kt + 2);
+      else
+        issue(Vh, voff, vbuf((s + 2) % 3), kt + 2);
+    }
   };
   auto wait_step = [&](int kt) {
-    const int n_new = (kt + 2 < kv_hi) + (kt + 1 < kv_hi);
-    if (n_new == 2)
-      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(2 * LPW));
-    else if (n_new == 1)
+    if (kt + 2 < kv_hi)
       __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(LPW));
     else
       __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
   };
 
-  // Every wave runs, for kt = kv_lo .. kv_hi: matrix phase kt (P V of block
-  // kt-1 and the scores of block kt), barrier, softmax phase kt, barrier.
-  // The trailing waves pass one barrier before their first step, the leading
+  // Every wave runs, for kt = kv_lo .. kv_hi: matrix phase kt (scores of
+  // block kt, P V of block kt-1), barrier, softmax phase kt, barrier.  The
+  // trailing waves pass one barrier before their first step, the leading
   // ones one after their last, so a trailing wave's matrix phase kt runs
   // beside the leading waves' softmax phase kt, and its softmax phase kt
   // beside their matrix phase kt+1.  In half steps h (the intervals between
   // consecutive barriers; h = 2(kt - kv_lo) is the leading waves' matrix
-  // phase kt): step kt's loads start at the beginning of h and are waited
-  // for at the end of h + 1, before the barrier.  Matrix phase kt reads
-  // K(kt) and V(kt-1) in h and h + 1; those slots are refilled at h + 2 at
-  // the earliest, after every wave has finished its LDS reads (lgkmcnt(0)
-  // before each barrier); the wait at the end of h + 1 makes K(kt+1) and
-  // V(kt), needed from h + 2 on, visible to every wave.
+  // phase kt): matrix phase kt reads K(kt) and V(kt-1) in h and h + 1;
+  // K(kt+2) is issued at the end of h + 1 and V(kt+2) at the end of h + 2,
+  // after every wave has finished its LDS reads of the slots they replace
+  // (lgkmcnt(0) before each barrier); K(kt+1) and V(kt+1), issued in the
+  // previous step, are waited for before the barriers that end h + 1 and
+  // h + 2, ahead of matrix phases kt+1 and kt+2 that read them.
   int cls_prev = FA_TILE_SKIP;
   auto step = [&](int kt, int s) {
     int cls_cur = FA_TILE_SKIP;
@@ -603,25 +608,27 @@ fa_fwd16_kernel(FaFwdParams p) {
         p.tiles[((size_t)bh * n_row_blocks + qb0 / FA_ROW_BLOCK) * n_key_blocks + kt] =
             (unsigned char)(cls_cur + 1);
     }
-    if (lead) issue_step(kt, s);
     phase_mfma(s, (s + 2) % 3);
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
     barrier_nofence();
     phase_softmax(kt, cls_cur);
-    if (lead) wait_step(kt);
+    issue_step(kt, s);
+    wait_step(kt);
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
     barrier_nofence();
     cls_prev = cls_cur;
   };
 
   // Every workgroup has at least one key block: row q0 < N always sees key
-  // q0 itself (the diagonal is visible under every mask).  Prologue: K of
-  // the first two blocks, V of the first, and zeros in the V slot that the
-  // first step's (probability 0) P V product reads.
+  // q0 itself (the diagonal is visible under every mask).  Prologue: K and V
+  // of the first two blocks, and zeros in the V slot that the first step's
+  // (probability 0) P V product reads.
   if (lead) {
     issue(Kh, koff, kbuf(0), kv_lo);
     if (kv_lo + 1 < kv_hi) issue(Kh, koff, kbuf(1), kv_lo + 1);
+  } else {
     issue(Vh, voff, vbuf(0), kv_lo);
+    if (kv_lo + 1 < kv_hi) issue(Vh, voff, vbuf(1), kv_lo + 1);
   }
 #pragma unroll
   for (int i = 0; i < TILEB / (NW * 64 * 16); ++i)
