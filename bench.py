@@ -21,6 +21,7 @@ Prints ONE JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--no-cpu-baseline] [--copy-calibration]
+       python bench.py --n-sweep   (traffic-vs-N evidence, bf16 causal B=1 H=32 d=128)
        python bench.py --record-traffic FETCH_CSV WRITE_CSV WORKLOAD "COMMAND"
 """
 from __future__ import annotations
@@ -232,6 +233,38 @@ def record_traffic(fetch_csv: str, write_csv: str, workload: str, command: str):
     print(json.dumps(rec["workloads"][workload]))
 
 
+def n_sweep(torch, fa):
+    """O(N) evidence: bf16 causal B=1 H=32 d=128 at N = 2048 .. 16384, seeded
+    N(0,1) inputs, two warm-up launches and one timed launch per N.  Under
+    rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE each N's dispatches are told apart
+    by their grid size (B*H*ceil(N/256) workgroups of 512 threads)."""
+    import numpy as np
+    for N in (2048, 4096, 8192, 16384):
+        rng = np.random.default_rng(2000 + N)
+        shape = (1, 32, N, 128)
+        q, k, v = (torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(torch.bfloat16).cuda()
+                   for _ in range(3))
+        o = torch.empty_like(q)
+        lse = torch.empty((1, 32, N), dtype=torch.float32, device=q.device)
+        stream = torch.cuda.current_stream()
+        call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), 1, 32, N, 128,
+                128 ** -0.5, fa.FA_MASK_CAUSAL, 0, fa.FA_DTYPE_BF16, fa.FA_DTYPE_BF16, stream.cuda_stream)
+        for _ in range(2):
+            fa.fa_fwd(*call)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = fa.fa_fwd(*call)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if st != fa.FA_OK:
+            raise fa.FaError(st, "fa_fwd")
+        ms = e0.elapsed_time(e1)
+        flops = 2.0 * 32 * N * N * 128
+        print(json.dumps({"sweep": "bf16 causal B=1 H=32 d=128", "N": N, "kernel_ms": round(ms, 4),
+                          "tflops": round(flops / ms / 1e9, 2),
+                          "grid_threads": 32 * ((N + 255) // 256) * 512}), flush=True)
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--record-traffic":
         # --record-traffic FETCH_CSV WRITE_CSV WORKLOAD "COMMAND"
@@ -244,6 +277,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--n-sweep", action="store_true",
+                    help="bf16 causal B=1 H=32 d=128 at N = 2048..16384 (one timed launch each)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU (each (batch, head) "
@@ -263,6 +298,9 @@ def main():
     fa.load()
     if args.copy_calibration:
         copy_calibration(torch)
+    if args.n_sweep:
+        n_sweep(torch, fa)
+        return
 
     q, k, v = si.make_workload(w)
     dev = "cuda:0"
