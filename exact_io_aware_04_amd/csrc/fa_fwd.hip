@@ -122,20 +122,6 @@ __device__ __forceinline__ fa_u32x2 pack4(float a, float b, float c, float d) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// acc + lo + hi of a packed pair of 16-bit values (one v_dot2c with (1, 1)).
-template <int DT>
-__device__ __forceinline__ float sum2(unsigned int pair, float acc) {
-  if constexpr (DT == 2) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
-  } else {
-    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
-  }
-}
-
 // Lanes l and l^32 hold the same query row: combine their values.  The swap
 // leaves each lane with its own value in one result and its partner's in the
 // other, so max / sum of the two results is the pair's max / sum.
@@ -281,7 +267,7 @@ __device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 *
 // transposing reads at rows 32kb + 16t + 4half + 0..3 and + 8 (the keys of
 // the P^T operand).
 #define FA_OPND_AHEAD 6
-template <int DT, int D, bool PV, bool QK>
+template <int DT, int D>
 __device__ __forceinline__ void matrix_phase(fa_f32x16 (&acc)[D / 32], fa_f32x16 (&sc)[2],
                                              fa_f32x16& lsum, const fa_f32x16& sc0,
                                              const fa_u32x4 (&pf)[2][2], const fa_u32x4 (&qf)[D / 16],
@@ -290,15 +276,13 @@ __device__ __forceinline__ void matrix_phase(fa_f32x16 (&acc)[D / 32], fa_f32x16
                                              const unsigned (&kread)[D / 16],
                                              const unsigned (&vread)[D / 32]) {
   constexpr int NCB = D / 32, NQF = D / 16, ROWB = 2 * D;
-  constexpr int NQK = QK ? 2 * NQF : 0;
-  constexpr int NOPS = NQK + (PV ? 4 * NCB : 0);
+  constexpr int NQK = 2 * NQF;
+  constexpr int NOPS = NQK + 4 * NCB;
   constexpr int R = FA_OPND_AHEAD;
   constexpr int NSLOT = R + 1;  // the slot being filled is never the one being read
   fa_u32x4 opnd[NSLOT];
-  if constexpr (QK) {
-    sc[0] = sc0;
-    sc[1] = sc0;
-  }
+  sc[0] = sc0;
+  sc[1] = sc0;
 #pragma unroll
   for (int i = 0; i < NOPS + R; ++i) {
     if (i >= R) {  // product i - R
@@ -326,16 +310,14 @@ __device__ __forceinline__ void matrix_phase(fa_f32x16 (&acc)[D / 32], fa_f32x16
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (PV) {
-    // row sums of the rounded probabilities: an all-ones A operand times the
-    // same P^T operands (every lane then holds its row's sum in every register)
-    constexpr unsigned ONE2 = DT == 2 ? 0x3F803F80u : 0x3C003C00u;
-    const fa_u32x4 ones = {ONE2, ONE2, ONE2, ONE2};
+  // row sums of the rounded probabilities: an all-ones A operand times the
+  // same P^T operands (every lane then holds its row's sum in every register)
+  constexpr unsigned ONE2 = DT == 2 ? 0x3F803F80u : 0x3C003C00u;
+  const fa_u32x4 ones = {ONE2, ONE2, ONE2, ONE2};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) lsum = mma16<DT>(ones, pf[kb][t], lsum);
-  }
+    for (int t = 0; t < 2; ++t) lsum = mma16<DT>(ones, pf[kb][t], lsum);
 }
 
 // Eight wavefronts, 32 query rows each, two per SIMD.  The two wavefronts of
@@ -487,7 +469,7 @@ fa_fwd16_kernel(FaFwdParams p) {
   // place): the probabilities of a skipped block are 0, which adds exactly
   // 0 to O, and the scores of a skipped block are never used.
   auto phase_mfma = [&](int ks, int vs) {
-    matrix_phase<DT, D, true, true>(acc, sc, lsum, sc0, pf, qf, kbuf(ks), vbuf(vs), kread, vread);
+    matrix_phase<DT, D>(acc, sc, lsum, sc0, pf, qf, kbuf(ks), vbuf(vs), kread, vread);
   };
   // Softmax phase of block kt (classification cls).
   // Softmax phase of block kt (classification cls).  Fast path (fully
