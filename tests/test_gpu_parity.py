@@ -174,6 +174,31 @@ def test_large_logits_stress(dtype):
             compare(o, lse, o_ref, lse_ref, dt, "stress x%g %s" % (mult, mask))
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 128), ("bf16", 64), ("f16", 64)])
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+def test_scores_rising_or_falling_along_the_keys(dtype, d, direction):
+    """Scores that climb by ~12 base-2 units per 64-key block (every block
+    exceeds the running reference by more than 2^8, so the kernel leaves its
+    fast path and rescales O block after block), or fall just as steeply
+    (later blocks underflow to 0 against the first block's maximum)."""
+    dt = DT[dtype]
+    N = 1000
+    say("monotone scores", dtype, d, direction)
+    q, k, v = si.make_qkv(1, 2, N, d, dtype, 77)
+    scale = 1.0 / math.sqrt(d)
+    j = torch.arange(N, dtype=torch.float32)
+    a = (j if direction == "rising" else (N - 1 - j)) * (12.0 / 64.0) / math.log2(math.e)
+    # q rows ~ ones(d) (+ small noise), k_j = a_j / (scale d) ones(d) + small noise:
+    # s_ij ~ a_j, i.e. 12 base-2 units more per 64 keys
+    ones = torch.ones(d)
+    qf = (ones + 0.01 * q.float()).to(dt)
+    kf = (a[None, None, :, None] / (scale * d) * ones + 0.01 * k.float()).to(dt)
+    for mask in ("none", "causal"):
+        o_ref, lse_ref = oracle.attention(qf, kf, v, scale, mask, 0)
+        o, lse = run(qf, kf, v, scale, mask, 0, torch.float32)
+        compare(o, lse, o_ref, lse_ref, dt, "%s %s" % (direction, mask))
+
+
 # ---------------------------------------------------------------------------
 # mask and tile-skip structure, exactly
 # ---------------------------------------------------------------------------
