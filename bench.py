@@ -15,7 +15,7 @@ Prints ONE JSON line:
               (2516.6 TFLOP/s: 256 CUs x 4096 FLOP/clk x 2.4 GHz); traffic =
               HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
               (scaled by a plain copy's reading), when the recorded counters
-              belong to the current kernel sources, else null
+              belong to the current kernel code (comments ignored), else null
   cpu_baseline the CPU oracle (fp64, OpenMP) timed on a bounded sample of the
               same workload's rows, in the same unit; context only
 
@@ -44,11 +44,64 @@ KERNEL_SOURCES = ["exact_io_aware_04_amd/csrc/fa_fwd.hip", "exact_io_aware_04_am
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.json")
 
 
+def code_text(src: str) -> str:
+    """C/C++/HIP source with its comments removed and each run of whitespace
+    collapsed to one newline (if the run holds one) or one space; string and
+    character literals are kept as written.  Two sources with the same code
+    text compile to the same program, so a comment edit does not void
+    counters taken on the kernel."""
+    out = []
+    i, n = 0, len(src)
+    pending = ""  # whitespace owed before the next token: "", " " or "\n"
+
+    def emit(t):
+        nonlocal pending
+        if pending and out:
+            out.append(pending)
+        pending = ""
+        out.append(t)
+
+    def owe(ws):
+        nonlocal pending
+        if ws == "\n" or not pending:
+            pending = ws
+
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j  # the newline itself is whitespace
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            if j < 0:
+                raise ValueError("unterminated block comment")
+            owe("\n" if "\n" in src[i:j] else " ")
+            i = j + 2
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            if j >= n:
+                raise ValueError("unterminated literal")
+            emit(src[i:j + 1])
+            i = j + 1
+        elif c.isspace():
+            owe("\n" if c == "\n" else " ")
+            i += 1
+        else:
+            emit(c)
+            i += 1
+    return "".join(out)
+
+
 def kernel_source_hash() -> str:
+    """SHA-256 of the kernel sources' code text (comments and layout
+    ignored)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode("utf-8"))
+        h.update(b"\0")
     return h.hexdigest()
 
 
@@ -281,9 +334,10 @@ def main():
                     help="bf16 causal B=1 H=32 d=128 at N = 2048..16384 (one timed launch each)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU (each (batch, head) "
-              "slice is independent; see the sharding notes in DESIGN.md); "
-              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        print("bench.py: runs on exactly one GPU; --gpus %d is not supported (every "
+              "(batch, head) slice is independent, so G GPUs would each run the same "
+              "kernel on B*H/G heads)" % args.gpus,
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

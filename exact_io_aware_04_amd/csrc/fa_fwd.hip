@@ -8,44 +8,57 @@
 // product with V run in one fused kernel that writes only the final result
 // (section "Samensmelting van bewerkingen in één CUDA-kernel").
 //
-// gfx950 mapping (one workgroup = 4 wavefronts of 64 lanes, 128 query rows,
-// two workgroups per CU):
+// gfx950 mapping, bf16/f16 inputs (one workgroup = 8 wavefronts of 64
+// lanes, 256 query rows, one workgroup per CU, two wavefronts per SIMD):
 //  * Each wavefront owns 32 query rows for the whole key loop.  Its Q rows
 //    stay in VGPRs as matrix-core operands, loaded once from HBM.
+//  * The two wavefronts of a SIMD run half a key block apart: while one
+//    issues its matrix products, the other computes its softmax, so the
+//    matrix core and the vector ALU are busy at the same time.  A workgroup
+//    barrier between half steps keeps the two groups (waves 0-3 and 4-7) in
+//    opposite phases.
 //  * K/V blocks of 64 keys go HBM -> LDS directly (buffer_load_dwordx4 with
-//    the LDS destination: no VGPR staging, no VALU), double-buffered: block
-//    t+1 is in flight while block t is computed, one barrier per block.  The
-//    buffer descriptor of each block ends at key N, so keys past the end read
-//    as zeros.  Rows are stored with an XOR swizzle of their 16-byte chunks
-//    (the swizzle is applied on the global side, since the LDS side of these
-//    loads is lane-contiguous) so that both LDS read patterns below run at
-//    the minimum number of LDS cycles.
+//    the LDS destination: no VGPR staging, no VALU) into rings of three
+//    slots each; block kt+2 is loaded while block kt is computed, K by the
+//    leading and V by the trailing wavefronts, each at the end of its
+//    softmax phase.  The buffer descriptor of each block ends at key N, so
+//    keys past the end read as zeros.  Rows are stored with an XOR swizzle of
+//    their 16-byte chunks (applied on the global side, since the LDS side of
+//    these loads is lane-contiguous) so that both LDS read patterns below
+//    run at the minimum number of LDS cycles.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_{bf16,f16}: in the 32x32 accumulator every lane then
 //    holds one query row (lane mod 32) and 16 of its keys, so the row max and
 //    row sum are in-lane reductions plus one exchange between the two lane
-//    halves (v_permlane32_swap).
+//    halves (v_permlane32_swap).  The accumulators start from -m/(scale
+//    log2 e) for the row's reference m, so each probability needs one
+//    multiply and one exponential.
 //  * O^T = V^T P^T: the probabilities are rounded to the input type and used
 //    straight from the accumulator registers as the B operand; the V^T
 //    operand is read from the row-major V block with ds_read_b64_tr_b16
 //    (within each 16-lane group, lane j receives element j mod 4 of the
 //    8-byte pieces addressed by lanes 4t + j/4, t = 0..3), at the keys that
 //    match the accumulator's row order, so no data moves between the two
-//    matrix products.
-//  * The softmax runs in base 2 with scale*log2(e) folded into one FMA.  The
-//    reference maximum is raised only when a row maximum exceeds it by more
-//    than 8 (base-2 units); in between, probabilities may reach 2^8, which
-//    fp32 accumulators and bf16/f16 operands hold exactly as well as values
-//    <= 1.  Output and row sum share the same reference, so the result is
-//    the same softmax; the O rescale is skipped on almost every block.
+//    matrix products.  The row sums of the rounded probabilities come from
+//    the matrix core too (an all-ones operand times the same P^T operands).
+//  * The softmax runs in base 2.  The reference maximum is set to the exact
+//    row maximum on a row's first block and on boundary blocks, and otherwise
+//    kept while every probability stays below 2^8 (checked through the lane
+//    sums); fp32 accumulators and bf16/f16 operands hold such values as
+//    exactly as values <= 1.  Output and row sum share the same reference,
+//    so the result is the same softmax; the O rescale is skipped on almost
+//    every block.
 //  * Tiles are classified with integer range tests (tile_class.h): fully
-//    masked key blocks are never visited, fully visible ones run without a
-//    per-element mask, only boundary blocks evaluate the mask predicate.
+//    masked key blocks are never visited by a workgroup, and give a wave
+//    probabilities of exactly 0 where only some of its rows see them; fully
+//    visible ones run without a per-element mask, only boundary blocks
+//    evaluate the mask predicate.
 //  * Work order: longest row tiles first for masked inputs, and, when
 //    batch*heads is a multiple of 8, every XCD (blockIdx mod 8) processes its
 //    own set of heads so that a head's K/V stays within one L2.
-// fp32 inputs use v_mfma_f32_32x32x2f32 in a simpler kernel of the same
-// structure (register-staged K/V, V row-major in LDS, 32-key blocks).
+// fp32 inputs use v_mfma_f32_32x32x2f32 in a simpler kernel (4 wavefronts,
+// 128 query rows, register-staged and double-buffered K/V, 32-key blocks,
+// the reference raised only when a row maximum exceeds it by more than 8).
 #include <hip/hip_runtime.h>
 
 #include "fa_kernels.h"
@@ -471,14 +484,13 @@ fa_fwd16_kernel(FaFwdParams p) {
   auto phase_mfma = [&](int ks, int vs) {
     matrix_phase<DT, D>(acc, sc, lsum, sc0, pf, qf, kbuf(ks), vbuf(vs), kread, vread);
   };
-  // Softmax phase of block kt (classification cls).
   // Softmax phase of block kt (classification cls).  Fast path (fully
   // visible block, row already started): p = 2^t straight from the scores;
-  // the row sums show whether any p exceeds 2^8 (a score more than 8 base-2
-  // units above the reference; the same laziness as the max test of the
-  // exact path).  Exact path (boundary block, a row's first block, or a
-  // lane's sum above 2^8, infinite or NaN): mask, row maximum, new reference
-  // at the exact maximum, rescale of O and the sums, probabilities again.
+  // a lane's sum of its 32 probabilities at most 2^8 bounds each of them by
+  // 2^8 (no score more than 8 base-2 units above the reference).  Exact path
+  // (boundary block, a row's first block, or a lane's sum above 2^8,
+  // infinite or NaN): mask, row maximum, new reference at the exact maximum,
+  // rescale of O and the sums, probabilities again.
   auto phase_softmax = [&](int kt, int cls) {
     if (cls == FA_TILE_SKIP) {
 #pragma unroll
@@ -581,7 +593,6 @@ fa_fwd16_kernel(FaFwdParams p) {
   // (lgkmcnt(0) before each barrier); K(kt+1) and V(kt+1), issued in the
   // previous step, are waited for before the barriers that end h + 1 and
   // h + 2, ahead of matrix phases kt+1 and kt+2 that read them.
-  int cls_prev = FA_TILE_SKIP;
   auto step = [&](int kt, int s) {
     int cls_cur = FA_TILE_SKIP;
     if (kt < kv_hi) {
@@ -598,7 +609,6 @@ fa_fwd16_kernel(FaFwdParams p) {
     wait_step(kt);
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
     barrier_nofence();
-    cls_prev = cls_cur;
   };
 
   // Every workgroup has at least one key block: row q0 < N always sees key
