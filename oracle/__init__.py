@@ -17,6 +17,9 @@ Two independent evaluations of the same definition live here:
   normalising exp(s) directly (no max subtraction): a different route to the
   same numbers, for tiny inputs only.
 
+``attention_gqa`` applies ``attention`` per query head when several query
+heads share one key/value head (``kv_head``: consecutive groups).
+
 Visibility of key j to query i: ``none`` all j; ``causal`` j <= i;
 ``sliding`` i - window < j <= i.
 """
@@ -109,6 +112,35 @@ def attention(q, k, v, scale: float, mask: str = "none", window: int = 0):
                                  _ptr(o), _ptr(lse))
     if rc != 0:
         raise RuntimeError("oracle_attn_f64 failed (%d)" % rc)
+    return o, lse
+
+
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """Key/value head read by query head h when H query heads share H_kv
+    key/value heads (H_kv divides H): consecutive groups of H / H_kv query
+    heads share one.  H_kv = 1 is multi-query attention (the extension named
+    in "FlashAttention (NL)", section "FlashAttention-2 (2023)"), H_kv = H
+    plain multi-head attention."""
+    return h // (H // H_kv)
+
+
+def attention_gqa(q, k, v, scale: float, mask: str = "none", window: int = 0):
+    """o, lse (fp64) for q [B, H, N, d] and k, v [B, H_kv, N, d]: every query
+    head h attends with key/value head kv_head(h, H, H_kv) of its batch
+    entry, by the same definition as ``attention``."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, H, N, d] and k, v [B, H_kv, N, d]")
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if k.shape[0] != B or k.shape[2:] != (N, d) or H_kv < 1 or H % H_kv:
+        raise ValueError("k, v must be [B, H_kv, N, d] with H_kv dividing H")
+    o = np.empty(q.shape, dtype=np.float64)
+    lse = np.empty(q.shape[:-1], dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head(h, H, H_kv)
+            o[b, h], lse[b, h] = attention(q[b, h], k[b, g], v[b, g], scale, mask, window)
     return o, lse
 
 

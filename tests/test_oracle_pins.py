@@ -13,7 +13,12 @@ Pins used (each independent of the oracle's own code):
     dominant logit, window of 1, window >= N;
   * invariants: key/value permutation, query permutation, slice
     independence, power-of-two scale folding, key shift (exact lse shift),
-    convex hull, and large-logit stability.
+    convex hull, and large-logit stability;
+  * shared key/value heads (multi-query attention, "FlashAttention (NL)",
+    section "FlashAttention-2 (2023)", and its grouped generalisation):
+    torch's fp64 scaled_dot_product_attention with its own head grouping,
+    mpmath brute force per query head, and a planted round-robin grouping
+    that the library pin must reject.
 """
 import math
 import os
@@ -274,3 +279,78 @@ def test_rejects_bad_arguments():
         oracle.attention(q, np.zeros((5, 2)), q, 1.0)
     with pytest.raises(RuntimeError):
         oracle.attention_rows(q, [0, 1, 2, 9], q, q, 1.0)
+
+
+# --------------------------------------------------------------------------
+# shared key/value heads (multi-query and grouped heads)
+# --------------------------------------------------------------------------
+GQA_CASES = [(4, 4), (4, 2), (6, 3), (6, 2), (8, 1), (3, 1)]  # (H, H_kv)
+
+
+def sdpa_gqa_fp64(q, k, v, scale, mask, window):
+    """torch's fp64 CPU scaled_dot_product_attention with its own grouping of
+    query heads over key/value heads (enable_gqa), and the matching lse."""
+    N = q.shape[-2]
+    vis = torch.from_numpy(visible_matrix(N, mask, window))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, attn_mask=vis, scale=scale, enable_gqa=True)
+    g = q.shape[1] // k.shape[1]
+    s = torch.matmul(q, k.repeat_interleave(g, dim=1).transpose(-1, -2)) * scale
+    lse = torch.logsumexp(s.masked_fill(~vis, float("-inf")), dim=-1)
+    return ref.numpy(), lse.numpy()
+
+
+@pytest.mark.parametrize("H,H_kv", GQA_CASES)
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 5)])
+def test_shared_kv_heads_match_torch_sdpa_fp64(H, H_kv, mask, window):
+    B, N, d = 2, 41, 8
+    q = torch.from_numpy(rand((B, H, N, d), 301 + H))
+    k = torch.from_numpy(rand((B, H_kv, N, d), 302 + H_kv))
+    v = torch.from_numpy(rand((B, H_kv, N, d), 303 + H_kv))
+    o, l = oracle.attention_gqa(q, k, v, 0.4, mask, window)
+    ro, rl = sdpa_gqa_fp64(q, k, v, 0.4, mask, window)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, rl, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 2)])
+def test_multi_query_heads_match_mpmath_bruteforce(mask, window):
+    # one key/value head shared by three query heads
+    N, d = 6, 3
+    q = rand((1, 3, N, d), 401, 1.5)
+    k, v = rand((1, 1, N, d), 402, 1.5), rand((1, 1, N, d), 403)
+    o, l = oracle.attention_gqa(q, k, v, 0.8, mask, window)
+    for h in range(3):
+        ob, lb = oracle.bruteforce_mp(q[0, h], k[0, 0], v[0, 0], 0.8, mask, window)
+        np.testing.assert_allclose(o[0, h], ob, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l[0, h], lb, rtol=0, atol=1e-12)
+
+
+def test_kv_head_grouping():
+    # consecutive query heads share a key/value head
+    assert [oracle.kv_head(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert [oracle.kv_head(h, 6, 3) for h in range(6)] == [0, 0, 1, 1, 2, 2]
+    assert {oracle.kv_head(h, 5, 1) for h in range(5)} == {0}
+    assert [oracle.kv_head(h, 4, 4) for h in range(4)] == [0, 1, 2, 3]
+
+
+def test_wrong_grouping_is_caught_by_the_library_pin(monkeypatch):
+    # plant round-robin grouping (h mod H_kv) in the oracle: the library
+    # routine's grouping must disagree
+    monkeypatch.setattr(oracle, "kv_head", lambda h, H, H_kv: h % H_kv)
+    B, H, H_kv, N, d = 1, 4, 2, 17, 8
+    q = torch.from_numpy(rand((B, H, N, d), 501))
+    k, v = torch.from_numpy(rand((B, H_kv, N, d), 502)), torch.from_numpy(rand((B, H_kv, N, d), 503))
+    o, _ = oracle.attention_gqa(q, k, v, 0.4, "causal", 0)
+    ro, _ = sdpa_gqa_fp64(q, k, v, 0.4, "causal", 0)
+    assert np.abs(o - ro).max() > 1e-3
+
+
+def test_shared_kv_heads_reject_bad_shapes():
+    q = np.zeros((1, 4, 5, 2))
+    with pytest.raises(ValueError):
+        oracle.attention_gqa(q, np.zeros((1, 3, 5, 2)), np.zeros((1, 3, 5, 2)), 1.0)
+    with pytest.raises(ValueError):
+        oracle.attention_gqa(q, np.zeros((1, 2, 6, 2)), np.zeros((1, 2, 6, 2)), 1.0)
+    with pytest.raises(ValueError):
+        oracle.attention_gqa(q, np.zeros((1, 2, 5, 2)), np.zeros((1, 1, 5, 2)), 1.0)
