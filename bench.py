@@ -20,6 +20,8 @@ Prints ONE JSON line:
               same workload's rows, in the same unit; context only
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       (NAME: one of seeded_inputs.BY_NAME, which includes the long-context
+       shape with shared key/value heads, fa_fwd_gqa)
        [--no-cpu-baseline] [--copy-calibration]
        python bench.py --n-sweep   (traffic-vs-N evidence, bf16 causal B=1 H=32 d=128)
        python bench.py --record-traffic FETCH_CSV WRITE_CSV WORKLOAD "COMMAND"
@@ -126,10 +128,12 @@ def step_flops(w) -> float:
 
 
 def algorithmic_bytes(w) -> int:
-    """Q, K, V read once, O written once (input dtype), lse written (fp32)."""
+    """Q, K, V read once, O written once (input dtype), lse written (fp32);
+    K and V have kv_heads heads."""
     esz = 4 if w.dtype == "f32" else 2
     n = w.B * w.H * w.N
-    return 4 * n * w.d * esz + 4 * n
+    n_kv = w.B * w.kv_heads * w.N
+    return (2 * n + 2 * n_kv) * w.d * esz + 4 * n
 
 
 def load_traffic(w):
@@ -167,10 +171,12 @@ def cpu_baseline(w, q, k, v, target_s: float = 12.0):
         return 4.0 * w.d * float(cnt.sum())
 
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    group = w.H // w.kv_heads
 
     def run(bh, rows):
         b, h = heads[bh]
-        qq, kk, vv = (t[b, h].double().numpy() for t in (q, k, v))
+        qq = q[b, h].double().numpy()
+        kk, vv = (t[b, h // group].double().numpy() for t in (k, v))
         t0 = time.perf_counter()
         oracle.attention_rows(qq[rows], rows, kk, vv, w.scale, w.mask, w.window)
         return time.perf_counter() - t0
@@ -363,14 +369,18 @@ def main():
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     dcode = {"f32": fa.FA_DTYPE_F32, "f16": fa.FA_DTYPE_F16, "bf16": fa.FA_DTYPE_BF16}[w.dtype]
-    call = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
-            w.B, w.H, w.N, w.d, float(w.scale), fa.MASKS[w.mask], int(w.window),
-            dcode, dcode, stream.cuda_stream)
+    ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr())
+    rest = (w.N, w.d, float(w.scale), fa.MASKS[w.mask], int(w.window), dcode, dcode,
+            stream.cuda_stream)
+    if w.kv_heads == w.H:
+        entry, call = fa.fa_fwd, ptrs + (w.B, w.H) + rest
+    else:
+        entry, call = fa.fa_fwd_gqa, ptrs + (w.B, w.H, w.kv_heads) + rest
 
     def step():
-        st = fa.fa_fwd(*call)
+        st = entry(*call)
         if st != fa.FA_OK:
-            raise fa.FaError(st, "fa_fwd")
+            raise fa.FaError(st, entry.__name__)
 
     for _ in range(args.warmup):
         step()
@@ -409,7 +419,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V, seed %d)" % w.seed,
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "N": w.N, "d": w.d,
                    "mask": w.mask, "window": w.window, "scale": w.scale,
                    "flops_per_step": flops, "pct_of_peak": round(100 * value / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,

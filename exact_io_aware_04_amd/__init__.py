@@ -1,7 +1,7 @@
 """Python binding of libfa.so: the fused exact attention forward pass on
 gfx950 (MI355X).
 
-The functions named like the C ABI (``fa_fwd``, ``fa_fwd_record_tiles``,
+The functions named like the C ABI (``fa_fwd``, ``fa_fwd_gqa``, ``fa_fwd_record_tiles``,
 ``fa_tile_shape``, ``fa_tile_map``, ``fa_status_string``, ``fa_last_error``,
 ``fa_probe_mfma``, ``fa_mfma_ceiling``) only marshal arguments: pointers are plain integers
 (device addresses, e.g. ``tensor.data_ptr()``), the stream is a hipStream_t
@@ -52,6 +52,8 @@ def load():
     ip = ctypes.POINTER(ctypes.c_int)
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp]
+    lib.fa_fwd_gqa.restype = i
     lib.fa_fwd_record_tiles.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, vp, vp]
     lib.fa_fwd_record_tiles.restype = i
     lib.fa_tile_shape.argtypes = [i, i, ip, ip, ip]
@@ -82,6 +84,12 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window, in_dtype,
            out_dtype, stream) -> int:
     return load().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window,
                          in_dtype, out_dtype, stream)
+
+
+def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, mask_kind, window, in_dtype,
+               out_dtype, stream) -> int:
+    return load().fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, mask_kind, window,
+                             in_dtype, out_dtype, stream)
 
 
 def fa_fwd_record_tiles(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window,
@@ -139,15 +147,20 @@ def _dtype_code(t):
 
 def attention(q, k, v, scale=None, mask: str = "none", window: int = 0,
               out_dtype=None, record_tiles=None):
-    """o, lse = softmax(scale q k^T + mask) v for device tensors [B, H, N, d].
+    """o, lse = softmax(scale q k^T + mask) v for device tensors q [B, H, N, d]
+    and k, v [B, H_kv, N, d]; H_kv = H is plain multi-head attention, a
+    smaller H_kv (dividing H) lets consecutive groups of H / H_kv query heads
+    share one key/value head (``fa_fwd_gqa``).
 
     ``out_dtype`` is the input dtype (default) or torch.float32.  ``lse`` is
     float32 [B, H, N].  ``record_tiles``: optional zero-filled uint8 device
-    tensor that receives the kernel's tile decisions (see fa.h).
+    tensor that receives the kernel's tile decisions (see fa.h; H_kv = H only).
     """
     import torch
-    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share one shape [B, H, N, d]")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, H, N, d] and k, v [B, H_kv, N, d]")
+    if (k.shape[0], k.shape[2], k.shape[3]) != (q.shape[0], q.shape[2], q.shape[3]):
+        raise ValueError("k, v must match q in B, N and d")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors")
     if not (q.dtype == k.dtype == v.dtype):
@@ -155,20 +168,27 @@ def attention(q, k, v, scale=None, mask: str = "none", window: int = 0,
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous [B, H, N, d]")
     B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if H_kv < 1 or H % H_kv:
+        raise ValueError("the key/value head count %d must divide H = %d" % (H_kv, H))
+    if record_tiles is not None and H_kv != H:
+        raise ValueError("record_tiles needs H_kv = H")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     o = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-            B, H, N, d, float(scale), MASKS[mask], int(window),
-            _dtype_code(q.dtype), _dtype_code(out_dtype))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr())
+    rest = (N, d, float(scale), MASKS[mask], int(window), _dtype_code(q.dtype),
+            _dtype_code(out_dtype))
     with torch.cuda.device(q.device):
-        if record_tiles is None:
-            st = fa_fwd(*args, stream)
+        if record_tiles is not None:
+            st = fa_fwd_record_tiles(*ptrs, B, H, *rest, record_tiles.data_ptr(), stream)
+        elif H_kv != H:
+            st = fa_fwd_gqa(*ptrs, B, H, H_kv, *rest, stream)
         else:
-            st = fa_fwd_record_tiles(*args, record_tiles.data_ptr(), stream)
+            st = fa_fwd(*ptrs, B, H, *rest, stream)
     if st != FA_OK:
         raise FaError(st, "fa_fwd")
     return o, lse

@@ -51,12 +51,14 @@ int keys_per_block(int in_dtype, int d) { return fa_keys_per_block(in_dtype, d);
 
 // Everything that can be decided without the device.
 int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
-               int B, int H, int N, int d, float scale, int mask_kind, int window,
-               int in_dtype, int out_dtype) {
+               int B, int H, int H_kv, int N, int d, float scale, int mask_kind,
+               int window, int in_dtype, int out_dtype) {
   if (!q || !k || !v || !o || !lse)
     return fail(FA_ERR_INVALID_ARG, "null pointer argument");
   if (B < 1 || H < 1 || N < 1)
     return fail(FA_ERR_INVALID_ARG, "B, H and N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0)
+    return fail(FA_ERR_INVALID_ARG, "H_kv must divide H = %d (got %d)", H, H_kv);
   if (N >= (1 << 30)) return fail(FA_ERR_INVALID_ARG, "N must be < 2^30 (got %d)", N);
   if (!valid_dtype(in_dtype)) return fail(FA_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
   if (!valid_dtype(out_dtype)) return fail(FA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
@@ -80,13 +82,15 @@ int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
   const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u;
   if (mis) return fail(FA_ERR_INVALID_ARG, "q, k, v, o must be 16-byte aligned");
   if (((uintptr_t)lse & 3u) != 0) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  const size_t nin = (size_t)bh * N * d * elem_bytes(in_dtype);
+  const size_t nq = (size_t)bh * N * d * elem_bytes(in_dtype);
+  const size_t nkv = (size_t)B * H_kv * N * d * elem_bytes(in_dtype);
   const size_t nout = (size_t)bh * N * d * elem_bytes(out_dtype);
   const size_t nlse = (size_t)bh * N * sizeof(float);
   const void* ins[3] = {q, k, v};
-  for (const void* in : ins) {
-    if (overlaps(o, nout, in, nin)) return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
-    if (overlaps(lse, nlse, in, nin)) return fail(FA_ERR_INVALID_ARG, "lse overlaps an input");
+  const size_t nins[3] = {nq, nkv, nkv};
+  for (int t = 0; t < 3; ++t) {
+    if (overlaps(o, nout, ins[t], nins[t])) return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
+    if (overlaps(lse, nlse, ins[t], nins[t])) return fail(FA_ERR_INVALID_ARG, "lse overlaps an input");
   }
   if (overlaps(o, nout, lse, nlse)) return fail(FA_ERR_INVALID_ARG, "o overlaps lse");
   return FA_OK;
@@ -116,10 +120,10 @@ int check_device() {
 }
 
 int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-            int H, int N, int d, float scale, int mask_kind, int window, int in_dtype,
-            int out_dtype, unsigned char* tiles, void* stream) {
-  int st = check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window, in_dtype,
-                      out_dtype);
+            int H, int H_kv, int N, int d, float scale, int mask_kind, int window,
+            int in_dtype, int out_dtype, unsigned char* tiles, void* stream) {
+  int st = check_args(q, k, v, o, lse, B, H, H_kv, N, d, scale, mask_kind, window,
+                      in_dtype, out_dtype);
   if (st != FA_OK) return st;
   st = check_device();
   if (st != FA_OK) return st;
@@ -131,6 +135,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   p.lse = lse;
   p.tiles = tiles;
   p.BH = B * H;
+  p.kv_group = H / H_kv;
   p.N = N;
   p.mask_kind = mask_kind;
   // a window of N or more keys is the causal mask; clamping keeps every
@@ -157,16 +162,23 @@ extern "C" {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
            int N, int d, float scale, int mask_kind, int window, int in_dtype, int out_dtype,
            void* stream) {
-  return run_fwd(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window, in_dtype, out_dtype,
-                 nullptr, stream);
+  return run_fwd(q, k, v, o, lse, B, H, H, N, d, scale, mask_kind, window, in_dtype,
+                 out_dtype, nullptr, stream);
+}
+
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+               int H, int H_kv, int N, int d, float scale, int mask_kind, int window,
+               int in_dtype, int out_dtype, void* stream) {
+  return run_fwd(q, k, v, o, lse, B, H, H_kv, N, d, scale, mask_kind, window, in_dtype,
+                 out_dtype, nullptr, stream);
 }
 
 int fa_fwd_record_tiles(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int H, int N, int d, float scale, int mask_kind, int window,
                         int in_dtype, int out_dtype, unsigned char* tiles, void* stream) {
   if (!tiles) return fail(FA_ERR_INVALID_ARG, "null tiles buffer");
-  return run_fwd(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window, in_dtype, out_dtype,
-                 tiles, stream);
+  return run_fwd(q, k, v, o, lse, B, H, H, N, d, scale, mask_kind, window, in_dtype,
+                 out_dtype, tiles, stream);
 }
 
 int fa_tile_shape(int d, int in_dtype, int* rows_per_workgroup, int* rows_per_wave,

@@ -381,10 +381,12 @@ fa_fwd16_kernel(FaFwdParams p) {
   const int qb1 = min(qb0 + FA_ROW_BLOCK, N);
   const int qi = qb0 + l32;
 
+  // query slice bh = b H + h reads key/value slice b H_kv + h / g = bh / g
   const size_t head_bytes = (size_t)N * ROWB;
+  const size_t kv_bytes = (size_t)(bh / p.kv_group) * head_bytes;
   const unsigned char* Qh = (const unsigned char*)p.q + (size_t)bh * head_bytes;
-  const unsigned char* Kh = (const unsigned char*)p.k + (size_t)bh * head_bytes;
-  const unsigned char* Vh = (const unsigned char*)p.v + (size_t)bh * head_bytes;
+  const unsigned char* Kh = (const unsigned char*)p.k + kv_bytes;
+  const unsigned char* Vh = (const unsigned char*)p.v + kv_bytes;
 
   int kv_lo, kv_hi;
   fa_key_block_range(q0, q1, BC, N, p.mask_kind, p.window, &kv_lo, &kv_hi);
@@ -671,9 +673,10 @@ fa_fwd32_kernel(FaFwdParams p) {
   const int qw1 = min(qw0 + FA_ROW_BLOCK, N);
   const int qi = qw0 + l32;
   const size_t head = (size_t)bh * N * D;
+  const size_t kv_head = (size_t)(bh / p.kv_group) * N * D;  // see the 16-bit kernel
   const float* Qh = (const float*)p.q + head;
-  const float* Kh = (const float*)p.k + head;
-  const float* Vh = (const float*)p.v + head;
+  const float* Kh = (const float*)p.k + kv_head;
+  const float* Vh = (const float*)p.v + kv_head;
 
   int kv_lo, kv_hi;
   fa_key_block_range(q0, q1, BC, N, p.mask_kind, p.window, &kv_lo, &kv_hi);

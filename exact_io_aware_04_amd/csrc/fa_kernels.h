@@ -12,6 +12,8 @@ struct FaFwdParams {
   float* lse;
   unsigned char* tiles;   // optional tile-decision record (nullptr: off)
   int BH;                 // batch * heads
+  int kv_group;           // query heads per key/value head (H / H_kv); the
+                          // K/V slice of query slice bh is bh / kv_group
   int N;                  // sequence length
   int mask_kind;          // FA_MASKK_*
   int window;             // sliding window (keys), >= 1 when sliding

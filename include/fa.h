@@ -87,6 +87,26 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int in_dtype, int out_dtype, void* stream);
 
 /*
+ * Same operation when several query heads share one key/value head: the
+ * multi-query attention that "FlashAttention (NL)", section
+ * "FlashAttention-2 (2023)", names among the extensions (H_kv = 1), and its
+ * grouped form (1 <= H_kv <= H, H_kv divides H).  Query head h of batch
+ * entry b attends with key/value head h / (H / H_kv) of that entry
+ * (consecutive groups of H / H_kv query heads share one):
+ *
+ *   s_ij = scale * <q[b,h,i,:], k[b,h/g,j,:]>,   o and lse as above, g = H/H_kv
+ *
+ *   q, o, lse  [B][H][N][d], [B][H][N][d], [B][H][N] as in fa_fwd
+ *   k, v       [B][H_kv][N][d] of in_dtype
+ * Every other argument, the arithmetic and the errors are those of fa_fwd
+ * (H_kv outside [1, H] or not dividing H: FA_ERR_INVALID_ARG).  fa_fwd is
+ * this call with H_kv = H.
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int H_kv, int N, int d, float scale, int mask_kind,
+               int window, int in_dtype, int out_dtype, void* stream);
+
+/*
  * Same as fa_fwd, and records the tile decisions the kernel took: for every
  * (b, h), row block rb of tile_rows rows and key block kb of tile_keys keys
  * (see fa_tile_shape), tiles[((b*H + h) * R + rb) * C + kb] is set to

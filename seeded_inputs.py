@@ -36,6 +36,11 @@ class Workload:
     window: int     # keys visible to a query under "sliding" (else 0)
     scale: float
     seed: int
+    H_kv: int = 0   # key/value heads (0: one per query head)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
 
 
 WORKLOADS = [
@@ -50,8 +55,16 @@ WORKLOADS = [
     Workload("swa_bf16_w4096_b1_h32_n32768_d128", 1, 32, 32768, 128, "bf16",
              "sliding", 4096, 1.0 / math.sqrt(128), 1004),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS}
 HEADLINE = WORKLOADS[3]
+# The long-context shape with key/value heads shared by groups of query heads
+# (4 query heads per key/value head, and one key/value head for all 32).
+SHARED_KV_WORKLOADS = [
+    Workload("longctx_gqa8_bf16_causal_b1_h32_n16384_d128", 1, 32, 16384, 128, "bf16",
+             "causal", 0, 1.0 / math.sqrt(128), 1005, H_kv=8),
+    Workload("longctx_mqa_bf16_causal_b1_h32_n16384_d128", 1, 32, 16384, 128, "bf16",
+             "causal", 0, 1.0 / math.sqrt(128), 1006, H_kv=1),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + SHARED_KV_WORKLOADS}
 
 
 def make_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int):
@@ -64,7 +77,19 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int):
     return tuple(out)
 
 
+def make_qkv_shared(B: int, H: int, H_kv: int, N: int, d: int, dtype: str, seed: int):
+    """q [B, H, N, d] and k, v [B, H_kv, N, d], same recipe and draw order."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for heads in (H, H_kv, H_kv):
+        x = rng.standard_normal((B, heads, N, d), dtype=np.float32)
+        out.append(torch.from_numpy(x).to(DTYPES[dtype]).contiguous())
+    return tuple(out)
+
+
 def make_workload(w: Workload):
+    if w.kv_heads != w.H:
+        return make_qkv_shared(w.B, w.H, w.kv_heads, w.N, w.d, w.dtype, w.seed)
     return make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed)
 
 

@@ -28,7 +28,7 @@ def call(**kw):
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fa.load()
     names = fa.declared_functions()
-    assert {"fa_fwd", "fa_fwd_record_tiles", "fa_tile_shape", "fa_tile_map",
+    assert {"fa_fwd", "fa_fwd_gqa", "fa_fwd_record_tiles", "fa_tile_shape", "fa_tile_map",
             "fa_status_string", "fa_last_error", "fa_probe_mfma", "fa_mfma_ceiling"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -124,3 +124,44 @@ def test_torch_wrapper_rejects_host_tensors():
     x = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         fa.attention(x, x, x)
+
+
+def call_gqa(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=8, H_kv=2, N=100, d=128, scale=0.1,
+                mask_kind=fa.FA_MASK_CAUSAL, window=0, in_dtype=fa.FA_DTYPE_BF16,
+                out_dtype=fa.FA_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_gqa(*(args[n] for n in ("q", "k", "v", "o", "lse", "B", "H", "H_kv", "N",
+                                             "d", "scale", "mask_kind", "window", "in_dtype",
+                                             "out_dtype", "stream")))
+
+
+@pytest.mark.parametrize("kw", [dict(H_kv=0), dict(H_kv=-2), dict(H_kv=3), dict(H_kv=9),
+                                dict(H=6, H_kv=4), dict(k=0), dict(N=0), dict(o=Q + 64)],
+                         ids=str)
+def test_shared_kv_invalid_arguments_are_rejected_on_the_host(kw):
+    assert call_gqa(**kw) == fa.FA_ERR_INVALID_ARG, fa.fa_last_error()
+
+
+def test_shared_kv_overlap_checks_use_the_key_value_head_count():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    # k holds B*H_kv*N*d bf16 = 2 * 100 * 128 * 2 bytes; o starting right
+    # after it does not overlap, o starting inside it does
+    kbytes = 2 * 100 * 128 * 2
+    st = call_gqa(o=K + kbytes)
+    assert st in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP), fa.fa_last_error()
+    assert call_gqa(o=K + kbytes - 16) == fa.FA_ERR_INVALID_ARG
+    # H_kv = H and H_kv = 1 are valid
+    assert call_gqa(H_kv=8) in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
+    assert call_gqa(H_kv=1) in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
+
+
+def test_torch_wrapper_rejects_mismatched_key_value_heads():
+    import torch
+    q = torch.zeros(1, 6, 8, 64)
+    with pytest.raises(ValueError):
+        fa.attention(q, torch.zeros(1, 4, 8, 64), torch.zeros(1, 4, 8, 64))
+    with pytest.raises(ValueError):
+        fa.attention(q, torch.zeros(1, 3, 9, 64), torch.zeros(1, 3, 9, 64))
