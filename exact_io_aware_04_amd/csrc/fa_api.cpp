@@ -78,7 +78,8 @@ int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
   const int rows_wg = fa_rows_per_wg(in_dtype, d);
   const long long tiles = bh * ((N + rows_wg - 1) / rows_wg);
   if (tiles > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "too many row tiles for one grid");
-  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
+  if (!fa_head_dim_built(in_dtype, d))
+    return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64, 128; 256 for f16/bf16)", d);
   const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u;
   if (mis) return fail(FA_ERR_INVALID_ARG, "q, k, v, o must be 16-byte aligned");
   if (((uintptr_t)lse & 3u) != 0) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
@@ -186,7 +187,8 @@ int fa_tile_shape(int d, int in_dtype, int* rows_per_workgroup, int* rows_per_wa
   if (!rows_per_workgroup || !rows_per_wave || !keys_per_block_out)
     return fail(FA_ERR_INVALID_ARG, "null output pointer");
   if (!valid_dtype(in_dtype)) return fail(FA_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
-  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
+  if (!fa_head_dim_built(in_dtype, d))
+    return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64, 128; 256 for f16/bf16)", d);
   *rows_per_workgroup = fa_rows_per_wg(in_dtype, d);
   *rows_per_wave = FA_ROW_BLOCK;
   *keys_per_block_out = keys_per_block(in_dtype, d);
@@ -201,7 +203,8 @@ int fa_tile_map(int N, int d, int in_dtype, int mask_kind, int window, unsigned 
     return fail(FA_ERR_INVALID_ARG, "unknown mask_kind %d", mask_kind);
   if (mask_kind == FA_MASK_SLIDING && window < 1)
     return fail(FA_ERR_INVALID_ARG, "sliding window must be >= 1 (got %d)", window);
-  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64, 128)", d);
+  if (!fa_head_dim_built(in_dtype, d))
+    return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64, 128; 256 for f16/bf16)", d);
   const int bc = keys_per_block(in_dtype, d);
   const int R = (N + FA_ROW_BLOCK - 1) / FA_ROW_BLOCK;
   const int C = (N + bc - 1) / bc;

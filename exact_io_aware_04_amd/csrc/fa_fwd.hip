@@ -258,11 +258,13 @@ __device__ __forceinline__ void store_output(const FaFwdParams& p, const fa_f32x
 // 16-byte chunk swizzles (chunk position = chunk ^ swizzle of the row).  K
 // rows are read 16 rows x one chunk per 16 lanes, V rows 8 rows x 4 chunks
 // per wavefront by the transposing read; each swizzle spreads every such
-// access over distinct chunk slots of the LDS banks.
+// access over distinct chunk slots of the LDS banks.  Rows of 128 and 256
+// elements start on the same bank, so both use the 128-element swizzle (it
+// flips chunk bits 0-3 and 2-3, staying inside each 16-chunk half row).
 template <int D>
-__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1)); }
+__device__ __forceinline__ int kswz(int r) { return D >= 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1)); }
 template <int D>
-__device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+__device__ __forceinline__ int vswz(int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 // Matrix phase of one wavefront: S^T = K Q^T over the current key block (QK)
 // and O^T += V^T P^T over the previous one (PV), as one software-pipelined
@@ -644,6 +646,294 @@ fa_fwd16_kernel(FaFwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 / f16 kernel, head dim 256
+// ---------------------------------------------------------------------------
+// Four wavefronts of 32 query rows, one per SIMD: at d = 256 a wave's output
+// accumulators alone take 128 registers (kept in AGPRs) and its Q fragments
+// 64, so two waves of this size do not fit on a SIMD and the ping-pong of
+// the kernel above is not available.  Each wave overlaps its own softmax
+// with its own matrix products instead.  Step kt: the score products of
+// block kt; then the P V products of block kt-1 (and its rounded row sums)
+// issued one by one between the instructions of block kt's fast softmax;
+// then, if needed, the exact path (which rescales O after the P V products
+// of block kt-1 have landed).  K and V are double-buffered in LDS
+// (128 KiB): at the top of step kt every wave issues its share of K(kt+1)
+// and V(kt), into the slots of K(kt-1) and V(kt-2), whose last readers
+// finished before the barrier that ended step kt-1.
+template <int DT, bool OUT_F32>
+__global__ void __launch_bounds__(FA_WAVES_WIDE * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fa_fwd16_wide_kernel(FaFwdParams p) {
+  constexpr int D = 256;
+  constexpr int NW = FA_WAVES_WIDE;
+  constexpr int ROWS_WG = NW * FA_ROW_BLOCK;
+  constexpr int BC = FA_KEYS_16;   // keys per block
+  constexpr int NKB = BC / 32;     // 32-key groups per block
+  constexpr int NCB = D / 32;      // 32-column output blocks
+  constexpr int NQF = D / 16;      // 16-deep slices of the QK^T contraction
+  constexpr int NQK = NKB * NQF;   // score products per block
+  constexpr int NPV = NKB * 2 * NCB;  // P V products per block
+  constexpr int ROWB = 2 * D;      // bytes of one K/V row
+  constexpr int TILEB = BC * ROWB; // bytes of one K or V block
+  constexpr int LPW = TILEB / (NW * 1024);  // one-kilobyte loads per wave per block
+  static_assert(NW == 4 && LPW == 8 && NKB == 2, "load layout below: 8 pieces of 2 rows per wave");
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[TILEB], ks1[TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs0[TILEB], vs1[TILEB];
+  auto kbuf = [&](int b) { return (FA_AS3 unsigned char*)(b == 0 ? ks0 : ks1); };
+  auto vbuf = [&](int b) { return (FA_AS3 unsigned char*)(b == 0 ? vs0 : vs1); };
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+  const int N = p.N;
+
+  int bh, q0;
+  work_item<ROWS_WG>(p, bh, q0);
+  const int q1 = min(q0 + ROWS_WG, N);
+  const int qb0 = q0 + wave * FA_ROW_BLOCK;
+  const int qb1 = min(qb0 + FA_ROW_BLOCK, N);
+  const int qi = qb0 + l32;
+
+  const size_t head_bytes = (size_t)N * ROWB;
+  const size_t kv_bytes = (size_t)(bh / p.kv_group) * head_bytes;
+  const unsigned char* Qh = (const unsigned char*)p.q + (size_t)bh * head_bytes;
+  const unsigned char* Kh = (const unsigned char*)p.k + kv_bytes;
+  const unsigned char* Vh = (const unsigned char*)p.v + kv_bytes;
+
+  int kv_lo, kv_hi;
+  fa_key_block_range(q0, q1, BC, N, p.mask_kind, p.window, &kv_lo, &kv_hi);
+
+  fa_u32x4 qf[NQF];  // q[qi][16 ks + 8 half .. +7]; rows past N read row N-1
+  {
+    const unsigned char* qrow = Qh + (size_t)min(qi, N - 1) * ROWB;
+#pragma unroll
+    for (int ks = 0; ks < NQF; ++ks) qf[ks] = *(const fa_u32x4*)(qrow + ks * 32 + half * 16);
+  }
+
+  // Loads: piece i (0..7) of wave w is rows r0 = 2w + 8(i mod 2) + 16(i/2)
+  // and r0 + 1 (lanes 0-31 and 32-63, 16 bytes each).  The swizzles depend
+  // on row bits 0-3 only, which 16(i/2) leaves unchanged: two global offsets
+  // per matrix serve all eight pieces, the rest goes into the scalar offset
+  // (which the descriptor's range check includes).
+  unsigned koff[2], voff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 2 * wave + 8 * j + half;
+    koff[j] = r * ROWB + 16 * (l32 ^ kswz<D>(r));
+    voff[j] = r * ROWB + 16 * (l32 ^ vswz<D>(r));
+  }
+  unsigned kread[NQF], vread[NCB];
+#pragma unroll
+  for (int s = 0; s < NQF; ++s) kread[s] = l32 * ROWB + 16 * ((2 * s + half) ^ kswz<D>(l32));
+  {
+    const int g = lane >> 4, t = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      vread[cb] = (4 * half + t) * ROWB + 64 * (cb ^ t) + 32 * (g & 1) + 8 * q;
+  }
+
+  // K or V block kt -> LDS slot (descriptor ends at key N: rows past N read 0)
+  auto issue = [&](const unsigned char* base, unsigned off0, unsigned off1,
+                   FA_AS3 unsigned char* dst, int kt) {
+    const int k0 = kt * BC;
+    const int nb = (min(N - k0, BC)) * ROWB;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * ROWB), 0, nb, FA_BUF_WORD3);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int r0 = 2 * wave + 8 * (i & 1) + 16 * (i >> 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_AS3 void*)(dst + r0 * ROWB), 16,
+                                               (int)((i & 1) ? off1 : off0), (i >> 1) * 16 * ROWB,
+                                               0, 0);
+    }
+  };
+
+  fa_f32x16 acc[NCB];  // O^T: acc[cb] holds columns 32cb.., row qi
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+    asm volatile("" : "+a"(acc[cb]));  // placement only: the matrix core's AGPRs
+  }
+  float m_ref = FA_NEG_INF, l_lane = 0.f;
+  fa_f32x16 lsum;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lsum[r] = 0.f;
+  const float c2 = p.scale_log2;
+  const float inv_c2 = 1.f / p.scale_log2;
+  const int n_row_blocks = (N + FA_ROW_BLOCK - 1) / FA_ROW_BLOCK;
+  const int n_key_blocks = (N + BC - 1) / BC;
+
+  // score accumulators start from -m_use / c2 (see the kernel above)
+  float sc_start = 0.f;
+  fa_f32x16 sc[NKB];
+  fa_u32x4 pf[NKB][2];  // rounded probabilities of the previous block
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) pf[kb][t] = fa_u32x4{0u, 0u, 0u, 0u};
+  constexpr unsigned ONE2 = DT == 2 ? 0x3F803F80u : 0x3C003C00u;
+  const fa_u32x4 ones = {ONE2, ONE2, ONE2, ONE2};
+
+  // One step (K slot s holds K(kt), V slot s holds V(kt-1)).
+  auto step = [&](int kt, int s) {
+    int cls = FA_TILE_SKIP;
+    if (kt < kv_hi) {
+      cls = fa_classify(qb0, qb1, kt * BC, BC, N, p.mask_kind, p.window);
+      if (p.tiles && lane == 0 && qb0 < N)
+        p.tiles[((size_t)bh * n_row_blocks + qb0 / FA_ROW_BLOCK) * n_key_blocks + kt] =
+            (unsigned char)(cls + 1);
+    }
+    if (kt + 1 < kv_hi) issue(Kh, koff[0], koff[1], kbuf(s ^ 1), kt + 1);
+    if (kt < kv_hi) issue(Vh, voff[0], voff[1], vbuf(s ^ 1), kt);
+
+    // S^T = K Q^T over block kt (stale and unused in the step after the last
+    // block); LDS operands read FA_OPND_AHEAD products ahead
+    {
+      constexpr int R = FA_OPND_AHEAD;
+      fa_u32x4 opnd[R + 1];
+      const FA_AS3 unsigned char* kcur = kbuf(s);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kb][r] = sc_start;
+#pragma unroll
+      for (int i = 0; i < NQK + R; ++i) {
+        if (i >= R) {
+          const int j = i - R;
+          sc[j % 2] = mma16<DT>(opnd[j % (R + 1)], qf[j / 2], sc[j % 2]);
+        }
+        if (i < NQK)
+          opnd[i % (R + 1)] = *(const FA_AS3 fa_u32x4*)(kcur + (i % 2) * 32 * ROWB + kread[i / 2]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // O^T += V^T P^T over block kt-1 (V slot s; probabilities 0 in the first
+    // step, whose slot holds zeros) and its rounded row sums, interleaved with
+    // the fast softmax of block kt: p = 2^t straight from the scores
+    float pr[NKB][16];
+    float psum = 0.f;
+    {
+      // V^T operand of product j (output block j mod NCB, keys of P^T
+      // operand (kb, t)), read FA_OPND_AHEAD products ahead
+      constexpr int R = FA_OPND_AHEAD;
+      fa_u32x4 opnd[R + 1];
+      const FA_AS3 unsigned char* vcur = vbuf(s);
+#pragma unroll
+      for (int i = 0; i < NPV + R; ++i) {
+        if (i < NPV) {
+          const int cb = i % NCB, kb = i / NCB / 2, t = i / NCB % 2;
+          const FA_AS3 unsigned char* vp = vcur + (32 * kb + 16 * t) * ROWB + vread[cb];
+          const fa_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_AS3 fa_i16x4*)vp);
+          const fa_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_AS3 fa_i16x4*)(vp + 8 * ROWB));
+          const fa_u32x2 l2 = __builtin_bit_cast(fa_u32x2, lo), h2 = __builtin_bit_cast(fa_u32x2, hi);
+          opnd[i % (R + 1)] = fa_u32x4{l2.x, l2.y, h2.x, h2.y};
+        }
+        if (i >= R) {
+          const int j = i - R, cb = j % NCB, kb = j / NCB / 2, t = j / NCB % 2;
+          acc[cb] = mma16<DT>(opnd[j % (R + 1)], pf[kb][t], acc[cb]);
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) lsum = mma16<DT>(ones, pf[kb][t], lsum);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          pr[kb][r] = exp2_hw(sc[kb][r] * c2);
+          psum += pr[kb][r];
+        }
+      // issue order: the first R operand reads, then per product one
+      // operand read R ahead, the product and a share of the softmax
+#pragma unroll
+      for (int j = 0; j < R; ++j) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int j = 0; j < NPV + 4; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix product
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+      }
+    }
+
+    const bool exact = cls == FA_TILE_PARTIAL || __ballot(m_ref == FA_NEG_INF) ||
+                       __ballot(!(psum <= 256.f));
+    if (cls == FA_TILE_SKIP) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) pf[kb][t] = fa_u32x4{0u, 0u, 0u, 0u};
+    } else {
+      if (exact) {
+        if (cls == FA_TILE_PARTIAL) apply_mask<NKB>(sc, kt * BC, qi, half, N, p.mask_kind, p.window);
+        const float m_use = m_ref == FA_NEG_INF ? 0.f : m_ref;
+        float mx = FA_NEG_INF;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+        mx = pair_max(mx) * c2;
+        const float m_new = fmaxf(m_ref, mx == FA_NEG_INF ? FA_NEG_INF : m_use + mx);
+        if (__ballot(m_new > m_ref)) {
+          // rescale O and the sums, which now hold block kt-1
+          const float alpha = m_new > m_ref ? (m_ref == FA_NEG_INF ? 0.f : exp2_hw(m_ref - m_new)) : 1.f;
+          l_lane *= alpha;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) lsum[r] *= alpha;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+        }
+        m_ref = m_new;
+        const float shift = m_ref == FA_NEG_INF ? 0.f : m_use - m_ref;
+        psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            pr[kb][r] = exp2_hw(__builtin_fmaf(sc[kb][r], c2, shift));
+            psum += pr[kb][r];
+          }
+        sc_start = m_ref == FA_NEG_INF ? 0.f : -m_ref * inv_c2;
+      }
+      // O is normalised by the sum of the rounded probabilities (on the
+      // matrix core), lse by the sum of the unrounded ones
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) pf[kb][t] = pack8<DT>(&pr[kb][8 * t]);
+      l_lane += psum;
+    }
+    // this step's loads have landed and every wave is done with its LDS
+    // reads before the next step reads them or overwrites the slots read here
+    __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
+    barrier_nofence();
+  };
+
+  // Every workgroup has at least one key block (the diagonal is visible).
+  // Prologue: K of the first block, and zeros in the V slot that the first
+  // step's (probability 0) P V products read.
+  issue(Kh, koff[0], koff[1], kbuf(0), kv_lo);
+#pragma unroll
+  for (int i = 0; i < TILEB / (NW * 64 * 16); ++i)
+    *(FA_AS3 fa_u32x4*)(vbuf(0) + (i * NW * 64 + tid) * 16) = fa_u32x4{0u, 0u, 0u, 0u};
+  static_assert(TILEB % (NW * 64 * 16) == 0, "zero fill must cover the slot");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = kv_lo;;) {
+    step(kt, 0);
+    if (++kt > kv_hi) break;
+    step(kt, 1);
+    if (++kt > kv_hi) break;
+  }
+  store_output<DT, D, OUT_F32>(p, acc, m_ref, pair_sum(l_lane), lsum[0], bh, qi, half);
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel (v_mfma_f32_32x32x2f32; one contraction element per lane)
 // ---------------------------------------------------------------------------
 template <int D>
@@ -824,6 +1114,9 @@ hipError_t launch(const FaFwdParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.BH * p.n_row_tiles));
   if constexpr (DT == 0)
     hipLaunchKernelGGL((fa_fwd32_kernel<D>), grid, dim3(FA_WAVES_32 * 64), 0, stream, p);
+  else if constexpr (D == 256)
+    hipLaunchKernelGGL((fa_fwd16_wide_kernel<DT, OUT_F32>), grid, dim3(FA_WAVES_WIDE * 64), 0,
+                       stream, p);
   else
     hipLaunchKernelGGL((fa_fwd16_kernel<DT, D, OUT_F32>), grid, dim3(FA_WAVES_16 * 64), 0, stream, p);
   return hipGetLastError();
@@ -839,9 +1132,11 @@ hipError_t fa_launch_fwd(int in_dtype, int out_dtype, int d, const FaFwdParams& 
       return d == 64 ? launch<0, 64, true>(p, stream) : launch<0, 128, true>(p, stream);
     case 1:
       if (d == 64) return of32 ? launch<1, 64, true>(p, stream) : launch<1, 64, false>(p, stream);
+      if (d == 256) return of32 ? launch<1, 256, true>(p, stream) : launch<1, 256, false>(p, stream);
       return of32 ? launch<1, 128, true>(p, stream) : launch<1, 128, false>(p, stream);
     default:
       if (d == 64) return of32 ? launch<2, 64, true>(p, stream) : launch<2, 64, false>(p, stream);
+      if (d == 256) return of32 ? launch<2, 256, true>(p, stream) : launch<2, 256, false>(p, stream);
       return of32 ? launch<2, 128, true>(p, stream) : launch<2, 128, false>(p, stream);
   }
 }

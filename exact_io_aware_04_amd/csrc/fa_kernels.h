@@ -28,6 +28,7 @@ struct FaFwdParams {
 constexpr int FA_ROW_BLOCK = 32;         // query rows per row block
 constexpr int FA_WAVES_32 = 4;           // wavefronts per workgroup, f32
 constexpr int FA_WAVES_16 = 8;           // wavefronts per workgroup, f16/bf16
+constexpr int FA_WAVES_WIDE = 4;         // wavefronts per workgroup, f16/bf16 at d = 256
 constexpr int FA_KEYS_16 = 64;           // keys per K/V block, f16/bf16
 constexpr int FA_KEYS_32 = 32;           // keys per K/V block, f32
 constexpr int FA_STAGES_16 = 3;          // depth of the K and V rings in LDS, f16/bf16
@@ -39,7 +40,12 @@ constexpr int fa_keys_per_block(int in_dtype, int d) {
 
 // query rows per workgroup for an input dtype code (0 = f32) and head dim
 constexpr int fa_rows_per_wg(int in_dtype, int d) {
-  return (in_dtype == 0 ? FA_WAVES_32 : FA_WAVES_16) * FA_ROW_BLOCK;
+  return (in_dtype == 0 ? FA_WAVES_32 : d == 256 ? FA_WAVES_WIDE : FA_WAVES_16) * FA_ROW_BLOCK;
+}
+
+// head dims built for an input dtype code: 64 and 128, and 256 for f16/bf16
+constexpr bool fa_head_dim_built(int in_dtype, int d) {
+  return d == 64 || d == 128 || (d == 256 && in_dtype != 0);
 }
 
 // dtype codes as in fa.h

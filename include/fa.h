@@ -71,7 +71,9 @@ enum {
  *   o          [B][H][N][d] of out_dtype (out_dtype == in_dtype, or F32)
  *   lse        [B][H][N] float
  *   B, H, N    >= 1, with B*H*N*d < 2^62 and N < 2^30
- *   d          64 or 128 (else FA_ERR_UNSUPPORTED)
+ *   d          64 or 128, and 256 for F16/BF16 inputs (the head size that
+ *              "FlashAttention (NL)", section "FlashAttention-2 (2023)",
+ *              names among the extensions); else FA_ERR_UNSUPPORTED
  *   scale      finite and >= 0 (1/sqrt(d) in the page's formula; 0 gives
  *              uniform weights over the visible keys)
  *   mask_kind  FA_MASK_*; window >= 1 when FA_MASK_SLIDING, ignored otherwise

@@ -64,7 +64,13 @@ SHARED_KV_WORKLOADS = [
     Workload("longctx_mqa_bf16_causal_b1_h32_n16384_d128", 1, 32, 16384, 128, "bf16",
              "causal", 0, 1.0 / math.sqrt(128), 1006, H_kv=1),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS + SHARED_KV_WORKLOADS}
+# Head dim 256: the long-context causal shape with half the heads (the same
+# number of FLOPs as the B=1 H=32 N=16384 d=128 workload).
+HEAD_DIM_256_WORKLOADS = [
+    Workload("longctx_bf16_causal_b1_h16_n16384_d256", 1, 16, 16384, 256, "bf16",
+             "causal", 0, 1.0 / math.sqrt(256), 1007),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + SHARED_KV_WORKLOADS + HEAD_DIM_256_WORKLOADS}
 
 
 def make_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int):

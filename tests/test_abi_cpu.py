@@ -71,11 +71,21 @@ def test_invalid_arguments_are_rejected_on_the_host(kw):
     assert fa.fa_last_error() != ""
 
 
-@pytest.mark.parametrize("d", [32, 96, 256])
+@pytest.mark.parametrize("d", [32, 96, 192, 512])
 def test_unbuilt_head_dims_are_unsupported(d):
     assert call(d=d) == fa.FA_ERR_UNSUPPORTED
     with pytest.raises(fa.FaError):
         fa.fa_tile_shape(d, fa.FA_DTYPE_BF16)
+
+
+def test_head_dim_256_is_built_for_16_bit_inputs_only():
+    assert call(d=256, in_dtype=fa.FA_DTYPE_F32, out_dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
+    with pytest.raises(fa.FaError):
+        fa.fa_tile_shape(256, fa.FA_DTYPE_F32)
+    import torch
+    if not torch.cuda.is_available():
+        for dt in (fa.FA_DTYPE_BF16, fa.FA_DTYPE_F16):
+            assert call(d=256, in_dtype=dt, out_dtype=dt) in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
 
 
 def test_valid_arguments_reach_the_device_check():
@@ -106,6 +116,8 @@ def test_tile_shape():
     assert fa.fa_tile_shape(128, fa.FA_DTYPE_BF16) == (256, 32, 64)
     assert fa.fa_tile_shape(64, fa.FA_DTYPE_F16) == (256, 32, 64)
     assert fa.fa_tile_shape(64, fa.FA_DTYPE_F32) == (128, 32, 32)
+    assert fa.fa_tile_shape(256, fa.FA_DTYPE_BF16) == (128, 32, 64)
+    assert fa.fa_tile_shape(256, fa.FA_DTYPE_F16) == (128, 32, 64)
 
 
 def test_tile_map_rejects_bad_arguments():

@@ -109,7 +109,8 @@ def sample_rows(N, rng, extra=64):
     return np.array(sorted({r for r in fixed + rnd if 0 <= r < N}), dtype=np.int64)
 
 
-@pytest.mark.parametrize("w", LARGE, ids=[w.name for w in LARGE])
+@pytest.mark.parametrize("w", LARGE + si.HEAD_DIM_256_WORKLOADS,
+                         ids=[w.name for w in LARGE + si.HEAD_DIM_256_WORKLOADS])
 def test_workload_sampled_rows(w):
     """Full-size launch (the benchmark's configuration); sampled rows of three
     heads checked one by one against the oracle."""
@@ -142,9 +143,11 @@ MASKS = [("none", 0), ("causal", 0), ("sliding", 1), ("sliding", 33), ("sliding"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("mask,window", MASKS)
 def test_ragged_sizes(dtype, d, mask, window):
+    if dtype == "f32" and d == 256:
+        pytest.skip("head dim 256 is built for 16-bit inputs only")
     dt = DT[dtype]
     for N in RAGGED_N:
         say("ragged", dtype, d, mask, window, N)
@@ -159,22 +162,24 @@ def test_ragged_sizes(dtype, d, mask, window):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_large_logits_stress(dtype):
+@pytest.mark.parametrize("d", [128, 256])
+def test_large_logits_stress(dtype, d):
     """Logit std 4 and 8: the running maximum moves often, many exps
     underflow."""
     dt = DT[dtype]
     for mult in (4.0, 8.0):
-        say("stress", dtype, mult)
-        q, k, v = si.make_qkv(1, 4, 700, 128, dtype, 42)
+        say("stress", dtype, d, mult)
+        q, k, v = si.make_qkv(1, 4, 700, d, dtype, 42)
         q = (q.float() * mult).to(dt)
-        scale = 1.0 / math.sqrt(128)
+        scale = 1.0 / math.sqrt(d)
         for mask, window in (("none", 0), ("causal", 0), ("sliding", 77)):
             o_ref, lse_ref = oracle.attention(q, k, v, scale, mask, window)
             o, lse = run(q, k, v, scale, mask, window, torch.float32)
             compare(o, lse, o_ref, lse_ref, dt, "stress x%g %s" % (mult, mask))
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 128), ("bf16", 64), ("f16", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 128), ("bf16", 64), ("f16", 64),
+                                     ("bf16", 256), ("f16", 256)])
 @pytest.mark.parametrize("direction", ["rising", "falling"])
 def test_scores_rising_or_falling_along_the_keys(dtype, d, direction):
     """Scores that climb by ~12 base-2 units per 64-key block (every block
@@ -207,7 +212,8 @@ PROBE = [(2048, "causal", 0), (2047, "causal", 0), (3000, "sliding", 4096),
          (16384, "causal", 0), (32768, "sliding", 4096), (16383, "sliding", 4095)]
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("bf16", 64), ("f32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("bf16", 64), ("f32", 64),
+                                     ("bf16", 256)])
 @pytest.mark.parametrize("N,mask,window", PROBE)
 def test_position_probe_recovers_visible_range(dtype, d, N, mask, window):
     if dtype == "f32" and N > 4096:
@@ -242,19 +248,19 @@ def brute_tiles(N, rows, keys, mask, window):
     return out
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("bf16", 256)])
 @pytest.mark.parametrize("N,mask,window", [(1000, "causal", 0), (1000, "sliding", 130),
                                            (777, "none", 0), (4096, "sliding", 1),
                                            (4096, "causal", 0), (129, "sliding", 64)])
-def test_kernel_tile_decisions(dtype, N, mask, window):
+def test_kernel_tile_decisions(dtype, d, N, mask, window):
     """The kernel's own record of skipped / full / partial blocks equals the
     brute-force map; key blocks outside a workgroup's range are never
     visited."""
-    say("tile record", dtype, N, mask, window)
+    say("tile record", dtype, d, N, mask, window)
     dt = DT[dtype]
-    wg_rows, rows, keys = fa.fa_tile_shape(128, fa._dtype_code(dt))
+    wg_rows, rows, keys = fa.fa_tile_shape(d, fa._dtype_code(dt))
     B, H = 2, 2
-    q, k, v = si.make_qkv(B, H, N, 128, dtype, 99)
+    q, k, v = si.make_qkv(B, H, N, d, dtype, 99)
     R, C = -(-N // rows), -(-N // keys)
     rec = torch.zeros(B * H * R * C, dtype=torch.uint8, device=DEV)
     o, lse = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV), 0.1, mask, window,
@@ -278,7 +284,8 @@ def test_kernel_tile_decisions(dtype, N, mask, window):
 # ---------------------------------------------------------------------------
 # closed forms and invariants on the device
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("f32", 128)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("f32", 128), ("bf16", 256),
+                                     ("f16", 256)])
 @pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 300)])
 def test_constant_values_and_zero_scale(dtype, d, mask, window):
     dt = DT[dtype]
@@ -303,11 +310,14 @@ def test_constant_values_and_zero_scale(dtype, d, mask, window):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-def test_window_special_cases(dtype):
+@pytest.mark.parametrize("d", [64, 256])
+def test_window_special_cases(dtype, d):
+    if dtype == "f32" and d == 256:
+        pytest.skip("head dim 256 is built for 16-bit inputs only")
     dt = DT[dtype]
-    N, d = 1300, 64
+    N = 1300
     q, k, v = si.make_qkv(1, 2, N, d, dtype, 321)
-    say("window 1", dtype)
+    say("window 1", dtype, d)
     o, lse = run(q, k, v, 0.125, "sliding", 1, torch.float32)
     s_ii = 0.125 * (q.double() * k.double()).sum(-1)
     compare(o, lse, v.double().numpy(), s_ii.numpy(), dt, "window 1")

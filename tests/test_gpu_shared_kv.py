@@ -48,9 +48,11 @@ MASKS = [("none", 0), ("causal", 0), ("sliding", 100)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("mask,window", MASKS)
 def test_shared_kv_heads_against_oracle(dtype, d, mask, window):
+    if dtype == "f32" and d == 256:
+        pytest.skip("head dim 256 is built for 16-bit inputs only")
     dt = DT[dtype]
     for (H, H_kv), N in zip(HEADS, [1, 65, 257, 1000]):
         say("shared kv", dtype, d, mask, window, "H", H, "H_kv", H_kv, "N", N)
@@ -64,7 +66,7 @@ def test_shared_kv_heads_against_oracle(dtype, d, mask, window):
             compare(o, lse, o_ref, lse_ref, dt, "H=%d H_kv=%d N=%d dtype-out" % (H, H_kv, N))
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("f32", 128)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("f32", 128), ("bf16", 256)])
 @pytest.mark.parametrize("H,H_kv", [(8, 1), (8, 2), (6, 3)])
 def test_shared_kv_heads_equal_copied_heads_bitwise(dtype, d, H, H_kv):
     N = 1000

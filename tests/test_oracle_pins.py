@@ -100,8 +100,9 @@ def test_matches_mpmath_bruteforce(N, d, mask, window):
 
 
 @pytest.mark.parametrize("mask,window", MASK_CASES + [("sliding", 64)])
-def test_matches_torch_sdpa_fp64(mask, window):
-    B, H, N, d = 2, 3, 97, 16
+@pytest.mark.parametrize("d", [16, 256])
+def test_matches_torch_sdpa_fp64(mask, window, d):
+    B, H, N = 2, 3, 97
     q, k, v = (torch.from_numpy(rand((B, H, N, d), s)) for s in (5, 6, 7))
     scale = 1.0 / math.sqrt(d)
     vis = torch.from_numpy(visible_matrix(N, mask, window))
