@@ -20,6 +20,10 @@ Two independent evaluations of the same definition live here:
 ``attention_gqa`` applies ``attention`` per query head when several query
 heads share one key/value head (``kv_head``: consecutive groups).
 
+``attention_bwd`` / ``attention_bwd_rows`` / ``attention_bwd_keys`` call
+``attn_bwd_oracle.c``: the gradients dq, dk, dv of the same definition for
+an output gradient do (chain rule written out, fp64).
+
 Visibility of key j to query i: ``none`` all j; ``causal`` j <= i;
 ``sliding`` i - window < j <= i.
 """
@@ -34,20 +38,30 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_BWD_SRC = os.path.join(_HERE, "attn_bwd_oracle.c")
+_BWD_LIB_PATH = os.path.join(_HERE, "libbwdoracle.so")
 
 MASKS = {"none": 0, "causal": 1, "sliding": 2}
 
 _lib = None
+_bwd_lib = None
+
+
+def _gcc(src: str, out: str) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+           "-Wall", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
 
 
 def build(force: bool = True) -> str:
-    """Compile attn_oracle.c with gcc (-O2, OpenMP, no fast-math)."""
+    """Compile attn_oracle.c and attn_bwd_oracle.c with gcc (-O2, OpenMP, no
+    fast-math) into two libraries."""
     if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-               "-Wall", "-o", tmp, _SRC, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB_PATH)
+        _gcc(_SRC, _LIB_PATH)
+    if force or not os.path.exists(_BWD_LIB_PATH):
+        _gcc(_BWD_SRC, _BWD_LIB_PATH)
     return _LIB_PATH
 
 
@@ -69,6 +83,21 @@ def bind(path: str):
     return lib
 
 
+def bind_bwd(path: str):
+    """Load a compiled backward-oracle library and declare its signatures."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lp = ctypes.POINTER(ctypes.c_longlong)
+    ll, dbl, i = ctypes.c_longlong, ctypes.c_double, ctypes.c_int
+    lib.oracle_attn_bwd_f64.argtypes = [dp, dp, dp, dp, ll, ll, ll, dbl, i, ll, dp, dp, dp]
+    lib.oracle_attn_bwd_f64.restype = i
+    lib.oracle_attn_bwd_rows_f64.argtypes = [dp, dp, dp, dp, ll, ll, dbl, i, ll, lp, ll, dp]
+    lib.oracle_attn_bwd_rows_f64.restype = i
+    lib.oracle_attn_bwd_keys_f64.argtypes = [dp, dp, dp, dp, ll, ll, dbl, i, ll, lp, ll, dp, dp]
+    lib.oracle_attn_bwd_keys_f64.restype = i
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
@@ -76,6 +105,15 @@ def _load():
             build(force=False)
         _lib = bind(_LIB_PATH)
     return _lib
+
+
+def _load_bwd():
+    global _bwd_lib
+    if _bwd_lib is None:
+        if not os.path.exists(_BWD_LIB_PATH):
+            build(force=False)
+        _bwd_lib = bind_bwd(_BWD_LIB_PATH)
+    return _bwd_lib
 
 
 def _f64(x) -> np.ndarray:
@@ -162,6 +200,61 @@ def attention_rows(q_rows, pos, k, v, scale: float, mask: str = "none",
     if rc != 0:
         raise RuntimeError("oracle_attn_rows_f64 failed (%d)" % rc)
     return o, lse
+
+
+def attention_bwd(q, k, v, do, scale: float, mask: str = "none", window: int = 0):
+    """dq, dk, dv (fp64) of plain attention for inputs shaped [..., N, d],
+    given the output gradient do: the chain rule of the definition, written
+    out in attn_bwd_oracle.c.  Leading dimensions are independent slices."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    if not (q.shape == k.shape == v.shape == do.shape) or q.ndim < 2:
+        raise ValueError("q, k, v, do must share one shape [..., N, d]")
+    N, d = q.shape[-2], q.shape[-1]
+    BH = int(np.prod(q.shape[:-2], dtype=np.int64)) if q.ndim > 2 else 1
+    dq, dk, dv = (np.empty(q.shape, dtype=np.float64) for _ in range(3))
+    rc = _load_bwd().oracle_attn_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(do), BH, N, d,
+                                         float(scale), MASKS[mask], int(window),
+                                         _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise RuntimeError("oracle_attn_bwd_f64 failed (%d)" % rc)
+    return dq, dk, dv
+
+
+def attention_bwd_rows(q, k, v, do, rows, scale: float, mask: str = "none",
+                       window: int = 0):
+    """dq[R, d] of query positions rows[R] of one [N, d] slice."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    N, d = q.shape
+    if k.shape != (N, d) or v.shape != (N, d) or do.shape != (N, d) or rows.ndim != 1:
+        raise ValueError("shape mismatch")
+    dq = np.empty((len(rows), d), dtype=np.float64)
+    rc = _load_bwd().oracle_attn_bwd_rows_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(do), N, d,
+                                              float(scale), MASKS[mask], int(window),
+                                              _ptr(rows, ctypes.c_longlong), len(rows),
+                                              _ptr(dq))
+    if rc != 0:
+        raise RuntimeError("oracle_attn_bwd_rows_f64 failed (%d)" % rc)
+    return dq
+
+
+def attention_bwd_keys(q, k, v, do, keys, scale: float, mask: str = "none",
+                       window: int = 0):
+    """dk[K, d], dv[K, d] of key positions keys[K] of one [N, d] slice."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    keys = np.ascontiguousarray(np.asarray(keys, dtype=np.int64))
+    N, d = q.shape
+    if k.shape != (N, d) or v.shape != (N, d) or do.shape != (N, d) or keys.ndim != 1:
+        raise ValueError("shape mismatch")
+    dk = np.empty((len(keys), d), dtype=np.float64)
+    dv = np.empty((len(keys), d), dtype=np.float64)
+    rc = _load_bwd().oracle_attn_bwd_keys_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(do), N, d,
+                                              float(scale), MASKS[mask], int(window),
+                                              _ptr(keys, ctypes.c_longlong), len(keys),
+                                              _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise RuntimeError("oracle_attn_bwd_keys_f64 failed (%d)" % rc)
+    return dk, dv
 
 
 def visible(i: int, j: int, mask: str, window: int) -> bool:
