@@ -1,7 +1,7 @@
 """Python binding of libfa.so: the fused exact attention forward pass on
 gfx950 (MI355X).
 
-The functions named like the C ABI (``fa_fwd``, ``fa_fwd_gqa``, ``fa_fwd_record_tiles``,
+The functions named like the C ABI (``fa_fwd``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_fwd_record_tiles``,
 ``fa_tile_shape``, ``fa_tile_map``, ``fa_status_string``, ``fa_last_error``,
 ``fa_probe_mfma``, ``fa_mfma_ceiling``) only marshal arguments: pointers are plain integers
 (device addresses, e.g. ``tensor.data_ptr()``), the stream is a hipStream_t
@@ -54,6 +54,8 @@ def load():
     lib.fa_fwd.restype = i
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp]
     lib.fa_fwd_gqa.restype = i
+    lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, i, i, vp]
+    lib.fa_bwd.restype = i
     lib.fa_fwd_record_tiles.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, vp, vp]
     lib.fa_fwd_record_tiles.restype = i
     lib.fa_tile_shape.argtypes = [i, i, ip, ip, ip]
@@ -90,6 +92,12 @@ def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, mask_kind, window, in_d
                out_dtype, stream) -> int:
     return load().fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, mask_kind, window,
                              in_dtype, out_dtype, stream)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, mask_kind, window,
+           dtype, stream) -> int:
+    return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, mask_kind,
+                         window, dtype, stream)
 
 
 def fa_fwd_record_tiles(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window,
@@ -192,3 +200,36 @@ def attention(q, k, v, scale=None, mask: str = "none", window: int = 0,
     if st != FA_OK:
         raise FaError(st, "fa_fwd")
     return o, lse
+
+
+def attention_bwd(q, k, v, o, lse, dout, scale=None, mask: str = "none", window: int = 0):
+    """dq, dk, dv of attention for device tensors [B, H, N, d] (f16/bf16):
+    q, k, v the forward inputs, o and lse its outputs (o in the input dtype),
+    dout the gradient of the loss with respect to o.  Allocates dq, dk, dv
+    and the float32 [B, H, N] workspace with torch and calls ``fa_bwd`` on
+    the current stream."""
+    import torch
+    if not (q.dim() == 4 and q.shape == k.shape == v.shape == o.shape == dout.shape):
+        raise ValueError("q, k, v, o, dout must share one shape [B, H, N, d]")
+    if lse.shape != q.shape[:3] or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, N]")
+    ts = (q, k, v, o, lse, dout)
+    if not all(t.is_cuda for t in ts):
+        raise ValueError("all tensors must be device tensors")
+    if not all(t.dtype == q.dtype for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o, dout must share one dtype")
+    if not all(t.is_contiguous() for t in ts):
+        raise ValueError("all tensors must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                    B, H, N, d, float(scale), MASKS[mask], int(window), _dtype_code(q.dtype), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

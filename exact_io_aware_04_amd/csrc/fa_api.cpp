@@ -156,9 +156,93 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   return ok();
 }
 
+int check_bwd_args(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                   float* delta, int B, int H, int N, int d, float scale, int mask_kind,
+                   int window, int dtype) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta)
+    return fail(FA_ERR_INVALID_ARG, "null pointer argument");
+  if (B < 1 || H < 1 || N < 1)
+    return fail(FA_ERR_INVALID_ARG, "B, H and N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if (N >= (1 << 30)) return fail(FA_ERR_INVALID_ARG, "N must be < 2^30 (got %d)", N);
+  if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL && mask_kind != FA_MASK_SLIDING)
+    return fail(FA_ERR_INVALID_ARG, "unknown mask_kind %d", mask_kind);
+  if (mask_kind == FA_MASK_SLIDING && window < 1)
+    return fail(FA_ERR_INVALID_ARG, "sliding window must be >= 1 (got %d)", window);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(FA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+  const long double total = (long double)B * H * N * d;
+  if (total >= 4.611686018427387904e18L)  // 2^62
+    return fail(FA_ERR_INVALID_ARG, "B*H*N*d too large");
+  const long long bh = (long long)B * H;
+  if (bh * ((N + FA_BWD_WAVES * 32 - 1) / (FA_BWD_WAVES * 32)) > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARG, "too many tiles for one grid");
+  if (dtype == FA_DTYPE_F32)
+    return fail(FA_ERR_UNSUPPORTED, "the backward pass is built for f16/bf16 inputs");
+  if (d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "backward head dim %d not built (64, 128)", d);
+  const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o |
+                         (uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u;
+  if (mis) return fail(FA_ERR_INVALID_ARG, "q, k, v, o, dout, dq, dk, dv must be 16-byte aligned");
+  if ((((uintptr_t)lse | (uintptr_t)delta) & 3u) != 0)
+    return fail(FA_ERR_INVALID_ARG, "lse and delta must be 4-byte aligned");
+  const size_t nm = (size_t)bh * N * d * elem_bytes(dtype);
+  const size_t nr = (size_t)bh * N * sizeof(float);
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const size_t nins[6] = {nm, nm, nm, nm, nm, nr};
+  const void* outs[4] = {dq, dk, dv, delta};
+  const size_t nouts[4] = {nm, nm, nm, nr};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (overlaps(outs[a], nouts[a], ins[b], nins[b]))
+        return fail(FA_ERR_INVALID_ARG, "an output of the backward pass overlaps an input");
+    for (int b = a + 1; b < 4; ++b)
+      if (overlaps(outs[a], nouts[a], outs[b], nouts[b]))
+        return fail(FA_ERR_INVALID_ARG, "outputs of the backward pass overlap");
+  }
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+           int d, float scale, int mask_kind, int window, int dtype, void* stream) {
+  int st = check_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale,
+                          mask_kind, window, dtype);
+  if (st != FA_OK) return st;
+  st = check_device();
+  if (st != FA_OK) return st;
+  FaBwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.delta = delta;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.BH = B * H;
+  p.N = N;
+  p.mask_kind = mask_kind;
+  p.window = mask_kind == FA_MASK_SLIDING ? (window < N ? window : N) : 0;
+  p.scale = scale;
+  // as in the forward call: scale = 0 becomes the smallest normal float,
+  // whose weights are uniform to fp32 precision
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  if (!(p.scale_log2 >= FLT_MIN)) p.scale_log2 = FLT_MIN;
+  p.n_row_tiles = (N + FA_BWD_WAVES * 32 - 1) / (FA_BWD_WAVES * 32);
+  p.heavy_first = mask_kind != FA_MASK_NONE ? 1 : 0;
+  hipError_t e = fa_launch_bwd(dtype, d, p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
            int N, int d, float scale, int mask_kind, int window, int in_dtype, int out_dtype,

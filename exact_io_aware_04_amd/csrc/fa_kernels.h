@@ -23,6 +23,29 @@ struct FaFwdParams {
   int heavy_first;        // 1: longest row tiles launched first (masks)
 };
 
+// Backward pass (fa_bwd.hip).
+struct FaBwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;       // gradient of the loss with respect to o
+  const float* lse;
+  float* delta;           // [BH][N]: receives <dout_i, o_i>
+  void* dq;
+  void* dk;
+  void* dv;
+  int BH;
+  int N;
+  int mask_kind;
+  int window;
+  float scale;
+  float scale_log2;       // scale * log2(e), at least FLT_MIN
+  int n_row_tiles;        // ceil(N / (FA_BWD_WAVES * 32)): query tiles = key tiles
+  int heavy_first;        // 1: longest query tiles of the dq pass first (masks)
+};
+constexpr int FA_BWD_WAVES = 4;
+
 // Tile geometry.  Work is skipped per row block of 32 query rows (one
 // 32x32 matrix-core tile of rows); each wavefront owns one row block.
 constexpr int FA_ROW_BLOCK = 32;         // query rows per row block
@@ -51,6 +74,7 @@ constexpr bool fa_head_dim_built(int in_dtype, int d) {
 // dtype codes as in fa.h
 hipError_t fa_launch_fwd(int in_dtype, int out_dtype, int d,
                          const FaFwdParams& p, hipStream_t stream);
+hipError_t fa_launch_bwd(int in_dtype, int d, const FaBwdParams& p, hipStream_t stream);
 hipError_t fa_launch_probe(int which, const void* a, const void* b, float* d,
                            hipStream_t stream);
 hipError_t fa_launch_mfma_ceiling(int n_blocks, int iters, unsigned long long* clk, float* sink,

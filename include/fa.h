@@ -109,6 +109,41 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                int window, int in_dtype, int out_dtype, void* stream);
 
 /*
+ * Backward pass of fa_fwd: the gradients dq, dk, dv of o with respect to q,
+ * k and v for an output gradient dout (of a loss L: dout = dL/do).  With
+ * P_ij the attention weights of fa_fwd (0 where masked):
+ *
+ *   dP_ij   = <dout[b,h,i,:], v[b,h,j,:]>
+ *   D_i     = sum_j P_ij dP_ij            (= <dout_i, o_i>)
+ *   dS_ij   = P_ij (dP_ij - D_i)
+ *   dq[b,h,i] = scale sum_j dS_ij k[b,h,j]
+ *   dk[b,h,j] = scale sum_i dS_ij q[b,h,i]
+ *   dv[b,h,j] = sum_i P_ij dout[b,h,i]
+ *
+ * P is recomputed tile by tile from q, k and the lse of the forward call
+ * rather than stored (the recomputation of "Memory-Optimized Flash Attention
+ * AI", section "How it works"); no N x N matrix is written.
+ *   q, k, v    [B][H][N][d] of dtype: the forward call's inputs
+ *   o, lse     the forward call's outputs ([B][H][N][d] of dtype, [B][H][N]
+ *              float)
+ *   dout       [B][H][N][d] of dtype
+ *   dq, dk, dv [B][H][N][d] of dtype: results
+ *   delta      [B][H][N] float, caller-owned workspace: receives D_i
+ *   B, H, N, scale, mask_kind, window: as passed to fa_fwd
+ *   d          64 or 128 (else FA_ERR_UNSUPPORTED)
+ *   dtype      FA_DTYPE_F16 or FA_DTYPE_BF16 (F32: FA_ERR_UNSUPPORTED)
+ * Results and delta must not overlap any input or each other; pointers
+ * 16-byte aligned (lse, delta 4-byte).  Arithmetic: products on the matrix
+ * cores in the input precision with fp32 accumulation; P and dS are rounded
+ * to the input precision before the products that use them.  Work is
+ * enqueued on `stream`; errors as for fa_fwd.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+           float* delta, int B, int H, int N, int d, float scale,
+           int mask_kind, int window, int dtype, void* stream);
+
+/*
  * Same as fa_fwd, and records the tile decisions the kernel took: for every
  * (b, h), row block rb of tile_rows rows and key block kb of tile_keys keys
  * (see fa_tile_shape), tiles[((b*H + h) * R + rb) * C + kb] is set to

@@ -83,6 +83,17 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int):
     return tuple(out)
 
 
+def make_qkv_dout(B: int, H: int, N: int, d: int, dtype: str, seed: int):
+    """q, k, v and an output gradient dout, all [B, H, N, d]: the same recipe
+    with a fourth draw."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(4):
+        x = rng.standard_normal((B, H, N, d), dtype=np.float32)
+        out.append(torch.from_numpy(x).to(DTYPES[dtype]).contiguous())
+    return tuple(out)
+
+
 def make_qkv_shared(B: int, H: int, H_kv: int, N: int, d: int, dtype: str, seed: int):
     """q [B, H, N, d] and k, v [B, H_kv, N, d], same recipe and draw order."""
     rng = np.random.default_rng(seed)

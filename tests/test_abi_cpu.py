@@ -28,7 +28,7 @@ def call(**kw):
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fa.load()
     names = fa.declared_functions()
-    assert {"fa_fwd", "fa_fwd_gqa", "fa_fwd_record_tiles", "fa_tile_shape", "fa_tile_map",
+    assert {"fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_fwd_record_tiles", "fa_tile_shape", "fa_tile_map",
             "fa_status_string", "fa_last_error", "fa_probe_mfma", "fa_mfma_ceiling"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -177,3 +177,46 @@ def test_torch_wrapper_rejects_mismatched_key_value_heads():
         fa.attention(q, torch.zeros(1, 4, 8, 64), torch.zeros(1, 4, 8, 64))
     with pytest.raises(ValueError):
         fa.attention(q, torch.zeros(1, 3, 9, 64), torch.zeros(1, 3, 9, 64))
+
+
+# backward pass: q k v o dout at A-spaced fake addresses, results further on
+DQ, DK, DV, DO_, LS, DL = 320 * A, 384 * A, 448 * A, 512 * A, 576 * A, 640 * A
+
+
+def call_bwd(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=LS, dout=DO_, dq=DQ, dk=DK, dv=DV, delta=DL, B=1, H=2,
+                N=100, d=128, scale=0.1, mask_kind=fa.FA_MASK_CAUSAL, window=0,
+                dtype=fa.FA_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_bwd(*(args[n] for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv",
+                                         "delta", "B", "H", "N", "d", "scale", "mask_kind",
+                                         "window", "dtype", "stream")))
+
+
+BWD_INVALID = [dict(q=0), dict(dout=0), dict(delta=0), dict(lse=0), dict(B=0), dict(N=-1),
+               dict(dtype=9), dict(mask_kind=5), dict(mask_kind=fa.FA_MASK_SLIDING, window=0),
+               dict(scale=float("nan")), dict(scale=-1.0), dict(dq=DQ + 8), dict(delta=DL + 2),
+               dict(dq=Q + 256),          # result overlaps an input
+               dict(delta=LS + 64),       # workspace overlaps lse
+               dict(dk=DQ + 4096),        # two results overlap
+               dict(dv=DL)]               # result overlaps the workspace
+
+
+@pytest.mark.parametrize("kw", BWD_INVALID, ids=str)
+def test_bwd_invalid_arguments_are_rejected_on_the_host(kw):
+    assert call_bwd(**kw) == fa.FA_ERR_INVALID_ARG, fa.fa_last_error()
+
+
+def test_bwd_unbuilt_cases_are_unsupported():
+    assert call_bwd(dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
+    assert call_bwd(d=256) == fa.FA_ERR_UNSUPPORTED
+    assert call_bwd(d=96) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_bwd_valid_arguments_reach_the_device_check():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    assert call_bwd() in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
+    assert call_bwd(d=64, dtype=fa.FA_DTYPE_F16, mask_kind=fa.FA_MASK_SLIDING,
+                    window=7) in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
