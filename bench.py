@@ -24,6 +24,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        shape with shared key/value heads, fa_fwd_gqa)
        [--no-cpu-baseline] [--copy-calibration]
        python bench.py --n-sweep   (traffic-vs-N evidence, bf16 causal B=1 H=32 d=128)
+       python bench.py --bwd       (backward pass, B=1 H=32 N=16384 d=128 bf16 causal)
        python bench.py --record-traffic FETCH_CSV WRITE_CSV WORKLOAD "COMMAND"
 """
 from __future__ import annotations
@@ -41,8 +42,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak (bf16 causal, N=16384, d=128)"
-KERNEL_SOURCES = ["exact_io_aware_04_amd/csrc/fa_fwd.hip", "exact_io_aware_04_amd/csrc/fa_kernels.h",
-                  "exact_io_aware_04_amd/csrc/tile_class.h", "exact_io_aware_04_amd/csrc/fa_api.cpp"]
+KERNEL_SOURCES = ["exact_io_aware_04_amd/csrc/fa_fwd.hip", "exact_io_aware_04_amd/csrc/fa_device.h",
+                  "exact_io_aware_04_amd/csrc/fa_kernels.h", "exact_io_aware_04_amd/csrc/tile_class.h",
+                  "exact_io_aware_04_amd/csrc/fa_api.cpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.json")
 
 
@@ -324,6 +326,60 @@ def n_sweep(torch, fa):
                           "grid_threads": 32 * ((N + 255) // 256) * 512}), flush=True)
 
 
+def bwd_bench(torch, fa, si, steps: int, warmup: int):
+    """Backward pass (fa_bwd: delta, dq and dk/dv kernels) on the long-context
+    shape B=1 H=32 N=16384 d=128, bf16, causal, seeded N(0,1) q, k, v and
+    output gradient, o and lse from one fa_fwd call.  FLOPs: 2.5 x the
+    forward's (five N x N x d products against two), the usual count; the
+    kernels issue 3.5 x (S and dP are formed in both loop kernels)."""
+    w = si.HEADLINE
+    q, k, v, do = si.make_qkv_dout(w.B, w.H, w.N, w.d, w.dtype, 1010)
+    dev = "cuda:0"
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.attention(qd, kd, vd, w.scale, w.mask, w.window)
+    dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+    delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    call = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            dod.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+            w.B, w.H, w.N, w.d, float(w.scale), fa.MASKS[w.mask], int(w.window),
+            fa.FA_DTYPE_BF16, stream.cuda_stream)
+
+    def step():
+        st = fa.fa_bwd(*call)
+        if st != fa.FA_OK:
+            raise fa.FaError(st, "fa_bwd")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    flops = 2.5 * step_flops(w)
+    avg = sum(ms) / len(ms)
+    peak = PEAK_TFLOPS[w.dtype]
+    print(json.dumps({
+        "metric": "attention bwd TFLOP/s (bf16 causal, N=16384, d=128)",
+        "value": round(flops * steps / wall / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(wall * 1e3 / steps, 4),
+        "higher_is_better": True, "dtype": w.dtype, "data": "synthetic (seeded N(0,1), seed 1010)",
+        "config": {"workload": "bwd_" + w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "mask": w.mask, "flops_per_step": flops, "flop_count": "2.5 x forward"},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (avg * 1e-3) / 1e12, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(flops / (avg * 1e-3) / 1e12 / peak, 4),
+                     "call_avg_ms": round(avg, 4), "call_min_ms": round(min(ms), 4),
+                     "note": "three kernels per call; per-kernel times from rocprofv3"}}),
+        flush=True)
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--record-traffic":
         # --record-traffic FETCH_CSV WRITE_CSV WORKLOAD "COMMAND"
@@ -336,6 +392,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (fa_bwd) on B=1 H=32 N=16384 d=128 bf16 causal")
     ap.add_argument("--n-sweep", action="store_true",
                     help="bf16 causal B=1 H=32 d=128 at N = 2048..16384 (one timed launch each)")
     args = ap.parse_args()
@@ -360,6 +418,9 @@ def main():
         copy_calibration(torch)
     if args.n_sweep:
         n_sweep(torch, fa)
+        return
+    if args.bwd:
+        bwd_bench(torch, fa, si, args.steps, args.warmup)
         return
 
     q, k, v = si.make_workload(w)
