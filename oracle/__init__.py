@@ -20,6 +20,9 @@ Two independent evaluations of the same definition live here:
 ``attention_gqa`` applies ``attention`` per query head when several query
 heads share one key/value head (``kv_head``: consecutive groups).
 
+``attention_decode`` evaluates a few queries at the last positions of a
+longer key/value cache (per (batch, head) through ``attention_rows``).
+
 ``attention_bwd`` / ``attention_bwd_rows`` / ``attention_bwd_keys`` call
 ``attn_bwd_oracle.c``: the gradients dq, dk, dv of the same definition for
 an output gradient do (chain rule written out, fp64).
@@ -199,6 +202,29 @@ def attention_rows(q_rows, pos, k, v, scale: float, mask: str = "none",
                                       MASKS[mask], int(window), _ptr(o), _ptr(lse))
     if rc != 0:
         raise RuntimeError("oracle_attn_rows_f64 failed (%d)" % rc)
+    return o, lse
+
+
+def attention_decode(q, k, v, scale: float, mask: str = "none", window: int = 0):
+    """o, lse (fp64) for q [B, H, Nq, d] against a key/value cache k, v
+    [B, H_kv, Nk, d] (Nq <= Nk): query i sits at position Nk - Nq + i, the
+    last Nq positions of the sequence the cache holds, and query head h reads
+    key/value head kv_head(h, H, H_kv); visibility as in ``attention`` at
+    those positions.  Nq = Nk is ``attention_gqa``."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H_kv, Nk, d]")
+    B, H, Nq, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d or H_kv < 1 or H % H_kv or Nq > Nk:
+        raise ValueError("k, v must be [B, H_kv, Nk, d] with H_kv dividing H and Nk >= Nq")
+    pos = np.arange(Nk - Nq, Nk, dtype=np.int64)
+    o = np.empty(q.shape, dtype=np.float64)
+    lse = np.empty(q.shape[:-1], dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head(h, H, H_kv)
+            o[b, h], lse[b, h] = attention_rows(q[b, h], pos, k[b, g], v[b, g], scale, mask, window)
     return o, lse
 
 

@@ -355,3 +355,49 @@ def test_shared_kv_heads_reject_bad_shapes():
         oracle.attention_gqa(q, np.zeros((1, 2, 6, 2)), np.zeros((1, 2, 6, 2)), 1.0)
     with pytest.raises(ValueError):
         oracle.attention_gqa(q, np.zeros((1, 2, 5, 2)), np.zeros((1, 1, 5, 2)), 1.0)
+
+
+# --------------------------------------------------------------------------
+# decoding: a few queries at the last positions of a longer cache
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 5), ("sliding", 40)])
+@pytest.mark.parametrize("H,H_kv", [(4, 4), (4, 1), (6, 2)])
+def test_decode_equals_the_last_rows_of_full_attention(mask, window, H, H_kv):
+    # the decode queries are the last Nq rows of a full-length query tensor
+    B, Nk, Nq, d = 2, 57, 3, 8
+    qfull = rand((B, H, Nk, d), 601)
+    k, v = rand((B, H_kv, Nk, d), 602), rand((B, H_kv, Nk, d), 603)
+    of, lf = oracle.attention_gqa(qfull, k, v, 0.45, mask, window)
+    od, ld = oracle.attention_decode(qfull[:, :, Nk - Nq:], k, v, 0.45, mask, window)
+    np.testing.assert_allclose(od, of[:, :, Nk - Nq:], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(ld, lf[:, :, Nk - Nq:], rtol=0, atol=1e-13)
+
+
+def test_decode_with_every_query_is_plain_attention():
+    q, k, v = rand((1, 2, 30, 4), 611), rand((1, 2, 30, 4), 612), rand((1, 2, 30, 4), 613)
+    for mask, window in (("none", 0), ("causal", 0), ("sliding", 4)):
+        od, ld = oracle.attention_decode(q, k, v, 0.7, mask, window)
+        of, lf = oracle.attention(q, k, v, 0.7, mask, window)
+        np.testing.assert_allclose(od, of, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(ld, lf, rtol=0, atol=1e-13)
+
+
+def test_decode_single_query_matches_mpmath():
+    # one query at the last position sees every key (causal) or the last W
+    Nk, d = 9, 3
+    q = rand((1, 1, 1, d), 621, 1.5)
+    k, v = rand((1, 1, Nk, d), 622, 1.5), rand((1, 1, Nk, d), 623)
+    for mask, window in (("causal", 0), ("sliding", 4)):
+        od, ld = oracle.attention_decode(q, k, v, 0.8, mask, window)
+        qfull = np.zeros((Nk, d))
+        qfull[-1] = q[0, 0, 0]
+        ob, lb = oracle.bruteforce_mp(qfull, k[0, 0], v[0, 0], 0.8, mask, window)
+        np.testing.assert_allclose(od[0, 0, 0], ob[-1], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(ld[0, 0, 0], lb[-1], rtol=0, atol=1e-12)
+
+
+def test_decode_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        oracle.attention_decode(np.zeros((1, 2, 5, 4)), np.zeros((1, 2, 4, 4)), np.zeros((1, 2, 4, 4)), 1.0)
+    with pytest.raises(ValueError):
+        oracle.attention_decode(np.zeros((1, 3, 1, 4)), np.zeros((1, 2, 4, 4)), np.zeros((1, 2, 4, 4)), 1.0)
