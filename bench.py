@@ -25,6 +25,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--no-cpu-baseline] [--copy-calibration]
        python bench.py --n-sweep   (traffic-vs-N evidence, bf16 causal B=1 H=32 d=128)
        python bench.py --bwd       (backward pass, B=1 H=32 N=16384 d=128 bf16 causal)
+       python bench.py --decode    (decoding, B=8 H=32 H_kv=8 Nq=1 Nk=32768 d=128 bf16)
        python bench.py --record-traffic FETCH_CSV WRITE_CSV WORKLOAD "COMMAND"
 """
 from __future__ import annotations
@@ -380,6 +381,74 @@ def bwd_bench(torch, fa, si, steps: int, warmup: int):
         flush=True)
 
 
+DECODE_SHAPE = dict(B=8, H=32, H_kv=8, Nq=1, Nk=32768, d=128)
+HBM_PEAK_GBS = 8000.0
+
+
+def decode_bytes(B, H, H_kv, Nq, Nk, d) -> int:
+    """Algorithmic bytes of one decode call: the key/value cache read once,
+    q read and o written (bf16), lse written (fp32)."""
+    return 2 * B * H_kv * Nk * d * 2 + 2 * B * H * Nq * d * 2 + B * H * Nq * 4
+
+
+def decode_bench(torch, fa, steps: int, warmup: int):
+    """Decoding against a key/value cache (fa_decode: split and merge
+    kernels): B=8 H=32 H_kv=8, one query per head at the end of a 32768-key
+    bf16 cache, d=128, causal, seeded N(0,1) inputs resident in HBM.  Bound by
+    HBM: reported in GB/s of algorithmic bytes against 8 TB/s."""
+    import numpy as np
+    c = DECODE_SHAPE
+    rng = np.random.default_rng(1020)
+    mk = lambda shape: torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(torch.bfloat16).cuda()
+    q = mk((c["B"], c["H"], c["Nq"], c["d"]))
+    k = mk((c["B"], c["H_kv"], c["Nk"], c["d"]))
+    v = mk((c["B"], c["H_kv"], c["Nk"], c["d"]))
+    o = torch.empty_like(q)
+    lse = torch.empty((c["B"], c["H"], c["Nq"]), dtype=torch.float32, device=q.device)
+    nb = fa.fa_decode_workspace_bytes(c["B"], c["H"], c["H_kv"], c["Nq"], c["Nk"], c["d"])
+    ws = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream()
+    scale = c["d"] ** -0.5
+    call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), c["B"], c["H"],
+            c["H_kv"], c["Nq"], c["Nk"], c["d"], scale, fa.FA_MASK_CAUSAL, 0, fa.FA_DTYPE_BF16,
+            ws.data_ptr(), nb, stream.cuda_stream)
+
+    def step():
+        st = fa.fa_decode(*call)
+        if st != fa.FA_OK:
+            raise fa.FaError(st, "fa_decode")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    avg = sum(ms) / len(ms)
+    nbytes = decode_bytes(**c)
+    flops = 4.0 * c["B"] * c["H"] * c["Nq"] * c["Nk"] * c["d"]
+    print(json.dumps({
+        "metric": "attention decode GB/s (bf16, B=8 H=32 H_kv=8, 1 query, 32768 cached keys, d=128)",
+        "value": round(nbytes * steps / wall / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(wall * 1e3 / steps, 4),
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic (seeded N(0,1), seed 1020)",
+        "config": dict(workload="decode_bf16_b8_h32_hkv8_nq1_nk32768_d128", mask="causal",
+                       bytes_per_step=nbytes, tflops=round(flops / (avg * 1e-3) / 1e12, 2), **c),
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "call_avg_ms": round(avg, 4), "call_min_ms": round(min(ms), 4),
+                     "note": "split and merge kernels per call; per-kernel times from rocprofv3"}}),
+        flush=True)
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--record-traffic":
         # --record-traffic FETCH_CSV WRITE_CSV WORKLOAD "COMMAND"
@@ -392,6 +461,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="time decoding (fa_decode) on B=8 H=32 H_kv=8 Nq=1 Nk=32768 d=128 bf16")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (fa_bwd) on B=1 H=32 N=16384 d=128 bf16 causal")
     ap.add_argument("--n-sweep", action="store_true",
@@ -421,6 +492,9 @@ def main():
         return
     if args.bwd:
         bwd_bench(torch, fa, si, args.steps, args.warmup)
+        return
+    if args.decode:
+        decode_bench(torch, fa, args.steps, args.warmup)
         return
 
     q, k, v = si.make_workload(w)

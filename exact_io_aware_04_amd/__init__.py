@@ -1,7 +1,8 @@
 """Python binding of libfa.so: the fused exact attention forward pass on
 gfx950 (MI355X).
 
-The functions named like the C ABI (``fa_fwd``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_fwd_record_tiles``,
+The functions named like the C ABI (``fa_fwd``, ``fa_fwd_gqa``, ``fa_decode``,
+``fa_decode_workspace_bytes``, ``fa_bwd``, ``fa_fwd_record_tiles``,
 ``fa_tile_shape``, ``fa_tile_map``, ``fa_status_string``, ``fa_last_error``,
 ``fa_probe_mfma``, ``fa_mfma_ceiling``) only marshal arguments: pointers are plain integers
 (device addresses, e.g. ``tensor.data_ptr()``), the stream is a hipStream_t
@@ -56,6 +57,10 @@ def load():
     lib.fa_fwd_gqa.restype = i
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, i, i, vp]
     lib.fa_bwd.restype = i
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = ctypes.c_longlong
+    lib.fa_decode.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, i, vp, ctypes.c_longlong, vp]
+    lib.fa_decode.restype = i
     lib.fa_fwd_record_tiles.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, vp, vp]
     lib.fa_fwd_record_tiles.restype = i
     lib.fa_tile_shape.argtypes = [i, i, ip, ip, ip]
@@ -98,6 +103,16 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, mask_kin
            dtype, stream) -> int:
     return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, mask_kind,
                          window, dtype, stream)
+
+
+def fa_decode_workspace_bytes(B, H, H_kv, Nq, Nk, d) -> int:
+    return load().fa_decode_workspace_bytes(B, H, H_kv, Nq, Nk, d)
+
+
+def fa_decode(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, mask_kind, window, dtype,
+              workspace, workspace_bytes, stream) -> int:
+    return load().fa_decode(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, mask_kind, window,
+                            dtype, workspace, workspace_bytes, stream)
 
 
 def fa_fwd_record_tiles(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window,
@@ -233,3 +248,40 @@ def attention_bwd(q, k, v, o, lse, dout, scale=None, mask: str = "none", window:
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def attention_decode(q, k, v, scale=None, mask: str = "causal", window: int = 0, workspace=None):
+    """o, lse for device tensors q [B, H, Nq, d] (the last Nq positions) and a
+    key/value cache k, v [B, H_kv, Nk, d] (f16/bf16).  Allocates o, lse and,
+    unless given (a uint8 device tensor), the workspace with torch, and calls
+    ``fa_decode`` on the current stream."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H_kv, Nk, d]")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, Nq, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k, v must match q in B and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = fa_decode_workspace_bytes(B, H, H_kv, Nq, Nk, d)
+    if nbytes < 0:
+        raise FaError(FA_ERR_INVALID_ARG, "fa_decode_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty((B, H, Nq, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       B, H, H_kv, Nq, Nk, d, float(scale), MASKS[mask], int(window),
+                       _dtype_code(q.dtype), workspace.data_ptr(), workspace.numel(), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_decode")
+    return o, lse

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = [os.path.join(CSRC, "fa_fwd.hip"), os.path.join(CSRC, "fa_bwd.hip"),
-           os.path.join(CSRC, "fa_api.cpp")]
+           os.path.join(CSRC, "fa_decode.hip"), os.path.join(CSRC, "fa_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU forms are turned off for all device code.

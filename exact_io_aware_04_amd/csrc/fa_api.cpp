@@ -3,6 +3,7 @@
 // dispatch to the gfx950 kernels, error reporting.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cfloat>
@@ -205,9 +206,137 @@ int check_bwd_args(const void* q, const void* k, const void* v, const void* o,
   return FA_OK;
 }
 
+// Split of the cache for fa_decode: the 32-key blocks from the first one any
+// query sees to the end, in n_chunks chunks of chunk_blocks blocks, about
+// 2048 work items (wavefronts) in all.
+struct DecodePlan {
+  int kb_lo, n_blocks, chunk_blocks, n_chunks;
+};
+DecodePlan decode_plan(int B, int H_kv, int Nq, int Nk, int mask_kind, int window) {
+  DecodePlan pl;
+  const int lo_key = mask_kind == FA_MASK_SLIDING ? std::max(0, Nk - Nq - window + 1) : 0;
+  pl.kb_lo = lo_key / FA_DECODE_KEYS;
+  pl.n_blocks = (Nk + FA_DECODE_KEYS - 1) / FA_DECODE_KEYS - pl.kb_lo;
+  const long long pairs = (long long)B * H_kv;
+  const long long want = std::max(1LL, std::min((long long)pl.n_blocks, (2048 + pairs - 1) / pairs));
+  pl.chunk_blocks = (int)((pl.n_blocks + want - 1) / want);
+  pl.n_chunks = (pl.n_blocks + pl.chunk_blocks - 1) / pl.chunk_blocks;
+  return pl;
+}
+
+long long decode_ws_bytes(int B, int H, int Nq, int d, int n_chunks) {
+  return (long long)n_chunks * B * H * Nq * (d + 1) * (long long)sizeof(float);
+}
+
+int check_decode_args(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int H_kv, int Nq, int Nk, int d, float scale, int mask_kind,
+                      int window, int dtype) {
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "null pointer argument");
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1)
+    return fail(FA_ERR_INVALID_ARG, "B, H, Nq and Nk must be >= 1");
+  if (Nq > Nk) return fail(FA_ERR_INVALID_ARG, "Nq (%d) must not exceed Nk (%d)", Nq, Nk);
+  if (Nk >= (1 << 30)) return fail(FA_ERR_INVALID_ARG, "Nk must be < 2^30");
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0)
+    return fail(FA_ERR_INVALID_ARG, "H_kv must divide H = %d (got %d)", H, H_kv);
+  if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL && mask_kind != FA_MASK_SLIDING)
+    return fail(FA_ERR_INVALID_ARG, "unknown mask_kind %d", mask_kind);
+  if (mask_kind == FA_MASK_SLIDING && window < 1)
+    return fail(FA_ERR_INVALID_ARG, "sliding window must be >= 1 (got %d)", window);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(FA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (d < 1) return fail(FA_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+  const long double big = (long double)B * H_kv * Nk * d + (long double)B * H * Nq * d;
+  if (big >= 4.611686018427387904e18L) return fail(FA_ERR_INVALID_ARG, "sizes too large");
+  if (dtype == FA_DTYPE_F32) return fail(FA_ERR_UNSUPPORTED, "decoding is built for f16/bf16");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "decode head dim %d not built (64, 128)", d);
+  if ((H / H_kv) * Nq > 32)
+    return fail(FA_ERR_UNSUPPORTED, "(H / H_kv) * Nq = %d rows per key/value head exceeds 32",
+                (H / H_kv) * Nq);
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u)
+    return fail(FA_ERR_INVALID_ARG, "q, k, v, o must be 16-byte aligned");
+  if (((uintptr_t)lse & 3u) != 0) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const size_t nq = (size_t)B * H * Nq * d * elem_bytes(dtype);
+  const size_t nkv = (size_t)B * H_kv * Nk * d * elem_bytes(dtype);
+  const size_t nl = (size_t)B * H * Nq * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  const size_t nins[3] = {nq, nkv, nkv};
+  for (int t = 0; t < 3; ++t) {
+    if (overlaps(o, nq, ins[t], nins[t])) return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
+    if (overlaps(lse, nl, ins[t], nins[t])) return fail(FA_ERR_INVALID_ARG, "lse overlaps an input");
+  }
+  if (overlaps(o, nq, lse, nl)) return fail(FA_ERR_INVALID_ARG, "o overlaps lse");
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+long long fa_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || Nq > Nk || H_kv < 1 || H_kv > H || H % H_kv != 0 ||
+      d < 1 || Nk >= (1 << 30)) {
+    fail(FA_ERR_INVALID_ARG, "invalid sizes");
+    return -1;
+  }
+  const DecodePlan pl = decode_plan(B, H_kv, Nq, Nk, FA_MASK_NONE, 0);
+  ok();
+  return decode_ws_bytes(B, H, Nq, d, pl.n_chunks);
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int H_kv, int Nq, int Nk, int d, float scale, int mask_kind, int window, int dtype,
+              void* workspace, long long workspace_bytes, void* stream) {
+  int st = check_decode_args(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, mask_kind, window,
+                             dtype);
+  if (st != FA_OK) return st;
+  const int win = mask_kind == FA_MASK_SLIDING ? (window < Nk ? window : Nk) : 0;
+  const DecodePlan pl = decode_plan(B, H_kv, Nq, Nk, mask_kind, win);
+  const long long need = decode_ws_bytes(B, H, Nq, d, pl.n_chunks);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARG, "workspace of %lld bytes needed (got %lld)", need,
+                workspace ? workspace_bytes : 0LL);
+  if (((uintptr_t)workspace & 15u) != 0)
+    return fail(FA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const size_t nq = (size_t)B * H * Nq * d * elem_bytes(dtype);
+  const size_t nkv = (size_t)B * H_kv * Nk * d * elem_bytes(dtype);
+  const size_t nl = (size_t)B * H * Nq * sizeof(float);
+  const void* all[5] = {q, k, v, o, lse};
+  const size_t nall[5] = {nq, nkv, nkv, nq, nl};
+  for (int t = 0; t < 5; ++t)
+    if (overlaps(workspace, (size_t)need, all[t], nall[t]))
+      return fail(FA_ERR_INVALID_ARG, "workspace overlaps an argument");
+  if ((long long)B * H_kv * pl.n_chunks > 0x7fffffffLL ||
+      (long long)B * H * Nq / (256 / (d / 4)) + 1 > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARG, "too many work items for one grid");
+  st = check_device();
+  if (st != FA_OK) return st;
+  FaDecodeParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.ws = (float*)workspace;
+  p.H = H;
+  p.H_kv = H_kv;
+  p.group = H / H_kv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.mask_kind = mask_kind;
+  p.window = win;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  if (!(p.scale_log2 >= FLT_MIN)) p.scale_log2 = FLT_MIN;
+  p.kb_lo = pl.kb_lo;
+  p.n_blocks = pl.n_blocks;
+  p.chunk_blocks = pl.chunk_blocks;
+  p.n_chunks = pl.n_chunks;
+  p.n_items = B * H_kv * pl.n_chunks;
+  p.rows = (long long)B * H * Nq;
+  hipError_t e = fa_launch_decode(dtype, d, p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,

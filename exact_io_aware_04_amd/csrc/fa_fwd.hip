@@ -177,16 +177,6 @@ __device__ __forceinline__ void store_output(const FaFwdParams& p, const fa_f32x
 // bf16 / f16 kernel
 // ---------------------------------------------------------------------------
 
-// 16-byte chunk swizzles (chunk position = chunk ^ swizzle of the row).  K
-// rows are read 16 rows x one chunk per 16 lanes, V rows 8 rows x 4 chunks
-// per wavefront by the transposing read; each swizzle spreads every such
-// access over distinct chunk slots of the LDS banks.  Rows of 128 and 256
-// elements start on the same bank, so both use the 128-element swizzle (it
-// flips chunk bits 0-3 and 2-3, staying inside each 16-chunk half row).
-template <int D>
-__device__ __forceinline__ int kswz(int r) { return D >= 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1)); }
-template <int D>
-__device__ __forceinline__ int vswz(int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 // Matrix phase of one wavefront: S^T = K Q^T over the current key block (QK)
 // and O^T += V^T P^T over the previous one (PV), as one software-pipelined

@@ -46,6 +46,32 @@ struct FaBwdParams {
 };
 constexpr int FA_BWD_WAVES = 4;
 
+// Decoding against a key/value cache (fa_decode.hip).
+struct FaDecodeParams {
+  const void* q;          // [B][H][Nq][D]
+  const void* k;          // [B][H_kv][Nk][D]
+  const void* v;
+  void* o;                // [B][H][Nq][D]
+  float* lse;             // [B][H][Nq]
+  float* ws;              // [n_chunks][rows][D] partial o, then [n_chunks][rows] partial lse
+  int H;
+  int H_kv;
+  int group;              // H / H_kv
+  int Nq;
+  int Nk;
+  int mask_kind;
+  int window;
+  float scale_log2;
+  int kb_lo;              // first 32-key block any query sees
+  int n_blocks;           // 32-key blocks from kb_lo to the end of the cache
+  int chunk_blocks;       // blocks per chunk
+  int n_chunks;
+  int n_items;            // B * H_kv * n_chunks work items (one wavefront each)
+  long long rows;         // B * H * Nq
+};
+constexpr int FA_DECODE_KEYS = 32;
+constexpr int FA_DECODE_WAVES = 4;
+
 // Tile geometry.  Work is skipped per row block of 32 query rows (one
 // 32x32 matrix-core tile of rows); each wavefront owns one row block.
 constexpr int FA_ROW_BLOCK = 32;         // query rows per row block
@@ -75,6 +101,7 @@ constexpr bool fa_head_dim_built(int in_dtype, int d) {
 hipError_t fa_launch_fwd(int in_dtype, int out_dtype, int d,
                          const FaFwdParams& p, hipStream_t stream);
 hipError_t fa_launch_bwd(int in_dtype, int d, const FaBwdParams& p, hipStream_t stream);
+hipError_t fa_launch_decode(int in_dtype, int d, const FaDecodeParams& p, hipStream_t stream);
 hipError_t fa_launch_probe(int which, const void* a, const void* b, float* d,
                            hipStream_t stream);
 hipError_t fa_launch_mfma_ceiling(int n_blocks, int iters, unsigned long long* clk, float* sink,

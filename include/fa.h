@@ -109,6 +109,32 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                int window, int in_dtype, int out_dtype, void* stream);
 
 /*
+ * Decoding against a key/value cache: Nq queries per head at the last Nq
+ * positions of a cache of Nk keys -- query i sits at position Nk - Nq + i
+ * and sees the keys fa_fwd's mask gives that position (causal: j <= Nk - Nq
+ * + i; sliding: the `window` keys up to it; none: all Nk).  Query head h
+ * reads key/value head h / (H / H_kv), as in fa_fwd_gqa; Nq = Nk is fa_fwd_gqa.
+ * The cache is split over the keys into chunks whose partial results
+ * (normalised o and lse per chunk) go to `workspace` and are merged with the
+ * online-softmax rescale of "FlashAttention (NL)", section "Online
+ * berekening van Softmax"; streaming a KV cache during generation is the
+ * workload of the engines named in section "Gespecialiseerde oplossingen".
+ *   q, o       [B][H][Nq][d] of dtype;  lse [B][H][Nq] float
+ *   k, v       [B][H_kv][Nk][d] of dtype
+ *   1 <= Nq <= Nk < 2^30;  (H / H_kv) * Nq <= 32 (else FA_ERR_UNSUPPORTED)
+ *   d          64 or 128;  dtype FA_DTYPE_F16 or FA_DTYPE_BF16
+ *   workspace  device memory of at least fa_decode_workspace_bytes(...)
+ *              bytes, 16-byte aligned, overlapping no other argument; its
+ *              contents on entry do not matter and are left undefined
+ * Other arguments, arithmetic and errors as for fa_fwd.
+ */
+long long fa_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d);
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int H_kv, int Nq, int Nk, int d, float scale,
+              int mask_kind, int window, int dtype, void* workspace,
+              long long workspace_bytes, void* stream);
+
+/*
  * Backward pass of fa_fwd: the gradients dq, dk, dv of o with respect to q,
  * k and v for an output gradient dout (of a loss L: dout = dL/do).  With
  * P_ij the attention weights of fa_fwd (0 where masked):

@@ -28,7 +28,7 @@ def call(**kw):
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fa.load()
     names = fa.declared_functions()
-    assert {"fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_fwd_record_tiles", "fa_tile_shape", "fa_tile_map",
+    assert {"fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_decode", "fa_decode_workspace_bytes", "fa_fwd_record_tiles", "fa_tile_shape", "fa_tile_map",
             "fa_status_string", "fa_last_error", "fa_probe_mfma", "fa_mfma_ceiling"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -220,3 +220,49 @@ def test_bwd_valid_arguments_reach_the_device_check():
     assert call_bwd() in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
     assert call_bwd(d=64, dtype=fa.FA_DTYPE_F16, mask_kind=fa.FA_MASK_SLIDING,
                     window=7) in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
+
+
+def test_decode_workspace_bytes():
+    # (H / H_kv) * Nq rows per key/value head, (d + 1) floats per row and chunk
+    nb = fa.fa_decode_workspace_bytes(8, 32, 8, 1, 32768, 128)
+    assert nb > 0 and nb % (8 * 32 * 1 * 129 * 4) == 0
+    chunks = nb // (8 * 32 * 129 * 4)
+    assert 1 <= chunks <= 32768 // 32
+    assert fa.fa_decode_workspace_bytes(1, 1, 1, 1, 1, 64) == 1 * 1 * 1 * 65 * 4
+    assert fa.fa_decode_workspace_bytes(1, 6, 4, 1, 100, 64) == -1   # H_kv must divide H
+    assert fa.fa_decode_workspace_bytes(1, 4, 4, 9, 8, 64) == -1     # Nq > Nk
+
+
+def call_decode(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=8, H_kv=2, Nq=1, Nk=1000, d=128, scale=0.1,
+                mask_kind=fa.FA_MASK_CAUSAL, window=0, dtype=fa.FA_DTYPE_BF16, ws=DQ,
+                ws_bytes=1 << 24, stream=None)
+    args.update(kw)
+    return fa.fa_decode(*(args[n] for n in ("q", "k", "v", "o", "lse", "B", "H", "H_kv", "Nq",
+                                            "Nk", "d", "scale", "mask_kind", "window", "dtype",
+                                            "ws", "ws_bytes", "stream")))
+
+
+DEC_INVALID = [dict(q=0), dict(Nq=0), dict(Nq=1001), dict(H_kv=3), dict(H_kv=0), dict(dtype=5),
+               dict(mask_kind=fa.FA_MASK_SLIDING, window=0), dict(scale=-1.0), dict(o=O + 2),
+               dict(ws=0), dict(ws_bytes=16), dict(ws=DQ + 8), dict(ws=K + 64), dict(o=K + 256)]
+
+
+@pytest.mark.parametrize("kw", DEC_INVALID, ids=str)
+def test_decode_invalid_arguments_are_rejected_on_the_host(kw):
+    assert call_decode(**kw) == fa.FA_ERR_INVALID_ARG, fa.fa_last_error()
+
+
+def test_decode_unbuilt_cases_are_unsupported():
+    assert call_decode(dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
+    assert call_decode(d=256) == fa.FA_ERR_UNSUPPORTED
+    assert call_decode(H=8, H_kv=1, Nq=5) == fa.FA_ERR_UNSUPPORTED   # 40 rows per key/value head
+
+
+def test_decode_valid_arguments_reach_the_device_check():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    assert call_decode() in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
+    assert call_decode(mask_kind=fa.FA_MASK_SLIDING, window=64, Nq=4, H=8, H_kv=1) in (
+        fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
