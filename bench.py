@@ -26,6 +26,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --n-sweep   (traffic-vs-N evidence, bf16 causal B=1 H=32 d=128)
        python bench.py --bwd       (backward pass, B=1 H=32 N=16384 d=128 bf16 causal)
        python bench.py --decode    (decoding, B=8 H=32 H_kv=8 Nq=1 Nk=32768 d=128 bf16)
+       python bench.py --hbm-reference   (torch sum / copy over 1 GiB, for context)
        python bench.py --record-traffic FETCH_CSV WRITE_CSV WORKLOAD "COMMAND"
 """
 from __future__ import annotations
@@ -449,6 +450,28 @@ def decode_bench(torch, fa, steps: int, warmup: int):
         flush=True)
 
 
+def hbm_reference(torch):
+    """Context for the HBM roofline: what torch's own kernels reach on this
+    device -- a sum over 1 GiB of bf16 (reads 1 GiB) and a 1 GiB device copy
+    (reads and writes 1 GiB) -- one JSON line each, ten timed calls."""
+    x = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").uniform_()
+    y = torch.empty_like(x)
+    for name, fn, nbytes in (("sum_bf16_1GiB", lambda: x.sum(), 1 << 30),
+                             ("copy_1GiB", lambda: y.copy_(x), 2 << 30)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        print(json.dumps({"hbm_reference": name, "ms": round(ms, 4),
+                          "GB_per_s": round(nbytes / ms / 1e6, 1)}), flush=True)
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--record-traffic":
         # --record-traffic FETCH_CSV WRITE_CSV WORKLOAD "COMMAND"
@@ -461,6 +484,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--hbm-reference", action="store_true",
+                    help="time torch's sum and copy over 1 GiB (context for the HBM roofline)")
     ap.add_argument("--decode", action="store_true",
                     help="time decoding (fa_decode) on B=8 H=32 H_kv=8 Nq=1 Nk=32768 d=128 bf16")
     ap.add_argument("--bwd", action="store_true",
@@ -495,6 +520,9 @@ def main():
         return
     if args.decode:
         decode_bench(torch, fa, args.steps, args.warmup)
+        return
+    if args.hbm_reference:
+        hbm_reference(torch)
         return
 
     q, k, v = si.make_workload(w)

@@ -208,7 +208,7 @@ int check_bwd_args(const void* q, const void* k, const void* v, const void* o,
 
 // Split of the cache for fa_decode: the 32-key blocks from the first one any
 // query sees to the end, in n_chunks chunks of chunk_blocks blocks, about
-// 2048 work items (wavefronts) in all.
+// 2048 work items (wavefronts) in all and at most 256 chunks.
 struct DecodePlan {
   int kb_lo, n_blocks, chunk_blocks, n_chunks;
 };
@@ -218,7 +218,8 @@ DecodePlan decode_plan(int B, int H_kv, int Nq, int Nk, int mask_kind, int windo
   pl.kb_lo = lo_key / FA_DECODE_KEYS;
   pl.n_blocks = (Nk + FA_DECODE_KEYS - 1) / FA_DECODE_KEYS - pl.kb_lo;
   const long long pairs = (long long)B * H_kv;
-  const long long want = std::max(1LL, std::min((long long)pl.n_blocks, (2048 + pairs - 1) / pairs));
+  const long long want =
+      std::max(1LL, std::min({(long long)pl.n_blocks, (2048 + pairs - 1) / pairs, 256LL}));
   pl.chunk_blocks = (int)((pl.n_blocks + want - 1) / want);
   pl.n_chunks = (pl.n_blocks + pl.chunk_blocks - 1) / pl.chunk_blocks;
   return pl;
@@ -307,7 +308,7 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
     if (overlaps(workspace, (size_t)need, all[t], nall[t]))
       return fail(FA_ERR_INVALID_ARG, "workspace overlaps an argument");
   if ((long long)B * H_kv * pl.n_chunks > 0x7fffffffLL ||
-      (long long)B * H * Nq / (256 / (d / 4)) + 1 > 0x7fffffffLL)
+      (long long)B * H * Nq / 4 + 1 > 0x7fffffffLL)
     return fail(FA_ERR_INVALID_ARG, "too many work items for one grid");
   st = check_device();
   if (st != FA_OK) return st;

@@ -16,11 +16,12 @@
 // independent wavefronts per workgroup, each with its own LDS (no workgroup
 // barrier).  Its 32 lanes of rows are the g = H / H_kv query heads x Nq
 // queries that read this key/value head (g Nq <= 32: one 32 x 32 matrix-core
-// tile), so every K/V byte is read once per key/value head.  32-key K and V
-// blocks stream HBM -> LDS (buffer_load_dwordx4 with the LDS destination,
-// double-buffered per wave) and are consumed as in the forward kernel: S^T =
-// K Q^T from 16-byte K row reads, O^T += V^T P^T with V^T from transposing
-// reads, row statistics in-lane plus one lane-half exchange.
+// tile), so every K/V byte is read once per key/value head.  The cache
+// streams in 32-key K and V blocks HBM -> LDS (buffer_load_dwordx4 with the
+// LDS destination) through rings of three slots per wave, two blocks ahead,
+// and is consumed as in the forward kernel: S^T = K Q^T from 16-byte K row
+// reads, O^T += V^T P^T with V^T from transposing reads, row statistics
+// in-lane plus one lane-half exchange.
 #include <hip/hip_runtime.h>
 
 #include "fa_device.h"
@@ -33,22 +34,35 @@ constexpr int DK = FA_DECODE_KEYS;   // keys per block
 constexpr int DW = FA_DECODE_WAVES;  // wavefronts (work items) per workgroup
 constexpr float LN2 = 0.69314718055994530942f;
 
-// one 32-key block of a [Nk][D] matrix -> LDS (rows past Nk read as zeros);
-// the wave loads it alone, one kilobyte (1024 / (2D) rows) per instruction
+// Descriptor of 32-key block kt of a [Nk][D] matrix: rows past Nk read as
+// zeros; a block at or past `kend` (the chunk's end) has size 0, so loads
+// of it read nothing and return zeros.  (The size and the block's row offset
+// are wave-uniform; readfirstlane states that, so the descriptor stays in
+// scalar registers.)
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const unsigned char* base, int kt,
+                                                             int kend, int Nk) {
+  constexpr int ROWB = 2 * D;
+  const int k0 = kt * DK;
+  const bool in = kt < kend && k0 < Nk;
+  const int nb = __builtin_amdgcn_readfirstlane(in ? min(Nk - k0, DK) * ROWB : 0);
+  const int r0 = __builtin_amdgcn_readfirstlane(in ? k0 : 0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)r0 * ROWB), 0, nb, FA_BUF_WORD3);
+}
+
+// K or V block kt -> LDS (K or V swizzle); the wave loads it alone, one
+// kilobyte (1024 / (2D) rows) per instruction
 template <int D, bool IS_K>
-__device__ __forceinline__ void load_block(const unsigned char* base, int kt, int Nk,
+__device__ __forceinline__ void load_block(const unsigned char* base, int kt, int kend, int Nk,
                                            FA_AS3 unsigned char* dst, int lane) {
   constexpr int ROWB = 2 * D, TILEB = DK * ROWB, RPP = 1024 / ROWB, CPR = ROWB / 16;
-  const int k0 = kt * DK;
-  const int nb = max(min(Nk - k0, DK), 0) * ROWB;
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(base + (k0 < Nk ? (size_t)k0 * ROWB : 0)), 0, nb, FA_BUF_WORD3);
+  const __amdgpu_buffer_rsrc_t rsrc = block_rsrc<D>(base, kt, kend, Nk);
 #pragma unroll
   for (int i = 0; i < TILEB / 1024; ++i) {
     const int r = i * RPP + lane / CPR, pos = lane % CPR;
     const int sw = IS_K ? kswz<D>(r) : vswz<D>(r);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_AS3 void*)(dst + i * 1024), 16,
-                                             r * ROWB + 16 * (pos ^ sw), 0, 0, 0);
+    const int off = r * ROWB + 16 * (pos ^ sw);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_AS3 void*)(dst + i * 1024), 16, off, 0, 0, 0);
   }
 }
 
@@ -63,7 +77,11 @@ __device__ __forceinline__ float rounded(float x) {
 template <int DT, int D>
 __global__ void __launch_bounds__(DW * 64) fa_decode_split_kernel(FaDecodeParams p) {
   constexpr int NCB = D / 32, NQF = D / 16, ROWB = 2 * D, TILEB = DK * ROWB;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[DW][4][TILEB];  // K0 K1 V0 V1
+  constexpr int LPB = TILEB / 1024;  // loads per block and matrix
+  // rings of three K and three V blocks per wave, one object per slot so
+  // that the compiler can tell the slot being read from the ones being filled
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[DW][TILEB], ks1[DW][TILEB],
+      ks2[DW][TILEB], vs0[DW][TILEB], vs1[DW][TILEB], vs2[DW][TILEB];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -90,10 +108,14 @@ __global__ void __launch_bounds__(DW * 64) fa_decode_split_kernel(FaDecodeParams
   const size_t kv = (size_t)bhk * Nk * ROWB;
   const unsigned char* Kh = (const unsigned char*)p.k + kv;
   const unsigned char* Vh = (const unsigned char*)p.v + kv;
-  FA_AS3 unsigned char* kb0 = (FA_AS3 unsigned char*)&lds[wave][0][0];
-  FA_AS3 unsigned char* kb1 = (FA_AS3 unsigned char*)&lds[wave][1][0];
-  FA_AS3 unsigned char* vb0 = (FA_AS3 unsigned char*)&lds[wave][2][0];
-  FA_AS3 unsigned char* vb1 = (FA_AS3 unsigned char*)&lds[wave][3][0];
+  FA_AS3 unsigned char* const kb0 = (FA_AS3 unsigned char*)&ks0[wave][0];
+  FA_AS3 unsigned char* const kb1 = (FA_AS3 unsigned char*)&ks1[wave][0];
+  FA_AS3 unsigned char* const kb2 = (FA_AS3 unsigned char*)&ks2[wave][0];
+  FA_AS3 unsigned char* const vb0 = (FA_AS3 unsigned char*)&vs0[wave][0];
+  FA_AS3 unsigned char* const vb1 = (FA_AS3 unsigned char*)&vs1[wave][0];
+  FA_AS3 unsigned char* const vb2 = (FA_AS3 unsigned char*)&vs2[wave][0];
+  auto kbuf = [&](int sl) { return sl == 0 ? kb0 : sl == 1 ? kb1 : kb2; };
+  auto vbuf = [&](int sl) { return sl == 0 ? vb0 : sl == 1 ? vb1 : vb2; };
 
   unsigned kread[NQF], vread[NCB];
 #pragma unroll
@@ -113,32 +135,28 @@ __global__ void __launch_bounds__(DW * 64) fa_decode_split_kernel(FaDecodeParams
   float m = FA_NEG_INF, l_lane = 0.f, lq_lane = 0.f;  // base-2 reference, unrounded / rounded sums
   const float c2 = p.scale_log2;
 
-  if (blo < bhi) {
-    load_block<D, true>(Kh, blo, Nk, kb0, lane);
-    load_block<D, false>(Vh, blo, Nk, vb0, lane);
-  }
-  for (int kt = blo; kt < bhi; ++kt) {
-    const int s = (kt - blo) & 1;
-    FA_AS3 unsigned char* kc = s ? kb1 : kb0;
-    FA_AS3 unsigned char* vc = s ? vb1 : vb0;
-    // the other slots were last read in the previous iteration by this wave
-    // alone, whose LDS reads completed before its products used them
-    if (kt + 1 < bhi) {
-      load_block<D, true>(Kh, kt + 1, Nk, s ? kb0 : kb1, lane);
-      load_block<D, false>(Vh, kt + 1, Nk, s ? vb0 : vb1, lane);
-      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(2 * TILEB / 1024));
-    } else {
-      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
-    }
+  // Block kt in slot sl.  At the top the wave issues K(kt+2) and V(kt+2) into
+  // the slots of block kt-1, read in the previous step; past the chunk's end
+  // these read nothing.  Every step issues the same loads, so one wait
+  // serves all: block kt, issued before block kt+1 and this step's loads,
+  // has landed once at most 4 x LPB loads are outstanding (loads complete in
+  // issue order).
+  auto step = [&](int kt, int sl) {
+    const int nx = (sl + 2) % 3;
+    load_block<D, true>(Kh, kt + 2, bhi, Nk, kbuf(nx), lane);
+    load_block<D, false>(Vh, kt + 2, bhi, Nk, vbuf(nx), lane);
+    __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(4 * LPB));
     const int cls = fa_classify(Nk - Nq, Nk, kt * DK, DK, Nk, p.mask_kind, p.window);
-    if (cls == FA_TILE_SKIP) continue;
+    if (cls == FA_TILE_SKIP) return;
+    const FA_AS3 unsigned char* kc = kbuf(sl);
+    const FA_AS3 unsigned char* vc = vbuf(sl);
     // S^T = K Q^T: s[r] is key kt*32 + 8(r/4) + 4half + r%4 of this lane's row
     fa_f32x16 sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < NQF; ++sl)
-      sc = mma16<DT>(*(const FA_AS3 fa_u32x4*)(kc + kread[sl]), qf[sl], sc);
+    for (int s = 0; s < NQF; ++s)
+      sc = mma16<DT>(*(const FA_AS3 fa_u32x4*)(kc + kread[s]), qf[s], sc);
     float t[16];
     float mx = FA_NEG_INF;
 #pragma unroll
@@ -187,6 +205,21 @@ __global__ void __launch_bounds__(DW * 64) fa_decode_split_kernel(FaDecodeParams
         const fa_u32x2 l2 = __builtin_bit_cast(fa_u32x2, lo), h2 = __builtin_bit_cast(fa_u32x2, hi);
         acc[cb] = mma16<DT>(fa_u32x4{l2.x, l2.y, h2.x, h2.y}, pf[tt], acc[cb]);
       }
+  };
+
+  if (blo < bhi) {
+    load_block<D, true>(Kh, blo, bhi, Nk, kb0, lane);
+    load_block<D, false>(Vh, blo, bhi, Nk, vb0, lane);
+    load_block<D, true>(Kh, blo + 1, bhi, Nk, kb1, lane);
+    load_block<D, false>(Vh, blo + 1, bhi, Nk, vb1, lane);
+    for (int kt = blo;;) {
+      step(kt, 0);
+      if (++kt >= bhi) break;
+      step(kt, 1);
+      if (++kt >= bhi) break;
+      step(kt, 2);
+      if (++kt >= bhi) break;
+    }
   }
   // chunk partial: o normalised by the rounded weights' sum, lse by the
   // unrounded one (as in the forward kernel); no visible key: o = 0, -inf
@@ -208,36 +241,54 @@ __global__ void __launch_bounds__(DW * 64) fa_decode_split_kernel(FaDecodeParams
         l_tot > 0.f ? (m + __log2f(l_tot)) * LN2 : FA_NEG_INF;
 }
 
-// Merge of the chunks: one row (batch, head, query) per D/4 threads.
+// Merge of the chunks: one wavefront per row (batch, head, query).  The
+// lanes first split the chunks (maximum and sum of exp(lse_c - max)), then
+// the columns (D / 64 each), summing the chunks' partial rows with weight
+// exp(lse_c - lse).
 template <int DT, int D>
 __global__ void __launch_bounds__(256) fa_decode_merge_kernel(FaDecodeParams p) {
-  constexpr int TPR = D / 4, RPB = 256 / TPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-  const int c4 = threadIdx.x % TPR;
-  if (row >= p.rows) return;  // no barrier in this kernel
+  constexpr int CPL = D / 64;  // columns per lane
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= p.rows) return;  // whole wavefront; no barrier in this kernel
   const float* wl = p.ws + (size_t)p.n_chunks * p.rows * D;
   float m = FA_NEG_INF;
-  for (int c = 0; c < p.n_chunks; ++c) m = fmaxf(m, wl[(size_t)c * p.rows + row]);
+  for (int c = lane; c < p.n_chunks; c += 64) m = fmaxf(m, wl[(size_t)c * p.rows + row]);
+#pragma unroll
+  for (int s = 32; s > 0; s >>= 1) m = fmaxf(m, __shfl_xor(m, s));
   float sum = 0.f;
-  fa_f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  if (m != FA_NEG_INF)
+    for (int c = lane; c < p.n_chunks; c += 64) sum += __expf(wl[(size_t)c * p.rows + row] - m);
+#pragma unroll
+  for (int s = 32; s > 0; s >>= 1) sum += __shfl_xor(sum, s);
+  float o[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) o[j] = 0.f;
   if (m != FA_NEG_INF) {
+    const float inv = 1.f / sum;
+#pragma unroll 4
     for (int c = 0; c < p.n_chunks; ++c) {
-      const float w = __expf(wl[(size_t)c * p.rows + row] - m);
-      const fa_f32x4 x = *(const fa_f32x4*)(p.ws + ((size_t)c * p.rows + row) * D + 4 * c4);
-      sum += w;
-      o += w * x;
+      const float w = __expf(wl[(size_t)c * p.rows + row] - m) * inv;
+      const float* x = p.ws + ((size_t)c * p.rows + row) * D + lane * CPL;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) o[j] += w * x[j];
     }
-    o *= 1.f / sum;
   }
-  *(fa_u32x2*)((unsigned char*)p.o + ((size_t)row * D + 4 * c4) * 2) = pack4<DT>(o[0], o[1], o[2], o[3]);
-  if (c4 == 0) p.lse[row] = m == FA_NEG_INF ? FA_NEG_INF : m + __logf(sum);
+  unsigned char* dst = (unsigned char*)p.o + ((size_t)row * D + lane * CPL) * 2;
+  if constexpr (CPL == 2) {
+    *(unsigned*)dst = __builtin_bit_cast(unsigned, pack4<DT>(o[0], o[1], 0.f, 0.f).x);
+  } else {
+    const fa_u32x2 h = pack4<DT>(o[0], 0.f, 0.f, 0.f);
+    *(unsigned short*)dst = (unsigned short)(h.x & 0xffffu);
+  }
+  if (lane == 0) p.lse[row] = m == FA_NEG_INF ? FA_NEG_INF : m + __logf(sum);
 }
 
 template <int DT, int D>
 hipError_t launch_decode(const FaDecodeParams& p, hipStream_t stream) {
   const unsigned g1 = (unsigned)((p.n_items + DW - 1) / DW);
   hipLaunchKernelGGL((fa_decode_split_kernel<DT, D>), dim3(g1), dim3(DW * 64), 0, stream, p);
-  const unsigned g2 = (unsigned)((p.rows + 256 / (D / 4) - 1) / (256 / (D / 4)));
+  const unsigned g2 = (unsigned)((p.rows + 3) / 4);
   hipLaunchKernelGGL((fa_decode_merge_kernel<DT, D>), dim3(g2), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -70,7 +70,7 @@ struct FaDecodeParams {
   long long rows;         // B * H * Nq
 };
 constexpr int FA_DECODE_KEYS = 32;
-constexpr int FA_DECODE_WAVES = 4;
+constexpr int FA_DECODE_WAVES = 3;
 
 // Tile geometry.  Work is skipped per row block of 32 query rows (one
 // 32x32 matrix-core tile of rows); each wavefront owns one row block.
