@@ -367,7 +367,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   // whose weights are uniform to fp32 precision
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   if (!(p.scale_log2 >= FLT_MIN)) p.scale_log2 = FLT_MIN;
-  p.n_row_tiles = (N + FA_BWD_WAVES * 32 - 1) / (FA_BWD_WAVES * 32);
+  p.n_q_tiles = (N + FA_BWD_DQ_WAVES * 32 - 1) / (FA_BWD_DQ_WAVES * 32);
+  p.n_k_tiles = (N + FA_BWD_WAVES * 32 - 1) / (FA_BWD_WAVES * 32);
   p.heavy_first = mask_kind != FA_MASK_NONE ? 1 : 0;
   hipError_t e = fa_launch_bwd(dtype, d, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));

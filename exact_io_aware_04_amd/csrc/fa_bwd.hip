@@ -11,7 +11,7 @@
 //   dq = scale dS k,   dk = scale dS^T q,   dv = P^T do.
 // Three kernels, launched in this order on one stream:
 //   fa_bwd_delta_kernel  D_i = <do_i, o_i> in fp32, one pass over do and o
-//   fa_bwd_dq_kernel     per 128-row query tile, over its key blocks:
+//   fa_bwd_dq_kernel     per 256-row query tile, over its key blocks:
 //                        S^T, dP^T, dS^T, dq^T += k^T dS^T   (lane = query)
 //   fa_bwd_dkdv_kernel   per 128-key tile, over its query blocks:
 //                        S, dP, dS, dv^T += do^T P, dk^T += q^T dS (lane = key)
@@ -19,8 +19,9 @@
 // query-block / key-block pair instead of five), so that no partial dq is
 // accumulated across workgroups.
 //
-// gfx950 mapping (both loop kernels): 4 wavefronts of 64 lanes, 32 rows (or
-// keys) each, one wavefront per SIMD; the resident operands (q and do rows,
+// gfx950 mapping: wavefronts of 64 lanes with 32 rows (or keys) each -- 8
+// per workgroup, two per SIMD, for dq; 4, one per SIMD with the two
+// accumulator sets in AGPRs, for dk/dv; the resident operands (q and do rows,
 // or k and v rows) stay in VGPRs as matrix-core fragments, the streamed
 // blocks (k and v, or q and do) go HBM -> LDS directly (buffer_load_dwordx4
 // with the LDS destination), double-buffered.  Every streamed block is read
@@ -35,7 +36,8 @@
 
 namespace {
 
-constexpr int BW = FA_BWD_WAVES;  // wavefronts per workgroup
+constexpr int BW = FA_BWD_WAVES;      // wavefronts per workgroup, dk/dv pass
+constexpr int BWQ = FA_BWD_DQ_WAVES;  // wavefronts per workgroup, dq pass
 constexpr int BR = 32;            // rows (or keys) per wavefront
 constexpr int BB = 64;            // rows (or keys) per streamed block
 constexpr float LOG2E = 1.44269504088896340736f;
@@ -115,20 +117,21 @@ __device__ __forceinline__ fa_u32x4 tr_operand(const FA_AS3 unsigned char* blk, 
 }
 
 // Block of 64 rows starting at row r0 of a [N][D] matrix -> LDS (rows past N
-// read as zeros).  Each of the BW wavefronts loads every BW-th kilobyte;
-// piece i lies BW kilobytes (16 rows at d = 128, 32 at d = 64) further, which
-// leaves bswz unchanged, so one global offset per lane serves all pieces.
-template <int D>
+// read as zeros).  Each of the NW wavefronts loads every NW-th kilobyte;
+// piece i lies NW kilobytes (a multiple of 16 rows) further, which leaves
+// bswz unchanged, so one global offset per lane serves all pieces.
+template <int D, int NW>
 __device__ __forceinline__ void load_block(const unsigned char* base, int r0, int N, unsigned off,
                                            FA_AS3 unsigned char* dst, int wave) {
-  constexpr int ROWB = 2 * D, TILEB = BB * ROWB, LPW = TILEB / (BW * 1024);
+  constexpr int ROWB = 2 * D, TILEB = BB * ROWB, LPW = TILEB / (NW * 1024);
+  static_assert(LPW >= 1 && LPW * NW * 1024 == TILEB, "pieces must cover the block");
   const int nb = max(min(N - r0, BB), 0) * ROWB;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(base + (r0 < N ? (size_t)r0 * ROWB : 0)), 0, nb, FA_BUF_WORD3);
 #pragma unroll
   for (int i = 0; i < LPW; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_AS3 void*)(dst + (i * BW + wave) * 1024), 16,
-                                             (int)off, i * BW * 1024, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_AS3 void*)(dst + (i * NW + wave) * 1024), 16,
+                                             (int)off, i * NW * 1024, 0, 0);
 }
 
 template <int D>
@@ -194,10 +197,12 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(FaBwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dq: one workgroup per (batch*head, 128-row query tile)
+// dq: one workgroup per (batch*head, 256-row query tile); eight wavefronts,
+// two per SIMD (the hardware overlaps one's VALU work with the other's
+// matrix products), sharing each K/V block in LDS
 // ---------------------------------------------------------------------------
 template <int DT, int D>
-__global__ void __launch_bounds__(BW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(BWQ * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_bwd_dq_kernel(FaBwdParams p) {
   constexpr int NKB = BB / 32, NCB = D / 32, NQF = D / 16, ROWB = 2 * D, TILEB = BB * ROWB;
   __shared__ __attribute__((aligned(1024))) unsigned char ks0[TILEB], ks1[TILEB];
@@ -210,8 +215,8 @@ fa_bwd_dq_kernel(FaBwdParams p) {
   const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
   const int N = p.N;
   const int bh = blockIdx.x % p.BH, rank = blockIdx.x / p.BH;
-  const int qt = p.heavy_first ? p.n_row_tiles - 1 - rank : rank;
-  const int q0 = qt * BW * BR, q1 = min(q0 + BW * BR, N);
+  const int qt = p.heavy_first ? p.n_q_tiles - 1 - rank : rank;
+  const int q0 = qt * BWQ * BR, q1 = min(q0 + BWQ * BR, N);
   const int qb0 = q0 + wave * BR, qb1 = min(qb0 + BR, N);
   const int qi = qb0 + l32, qr = min(qi, N - 1);
 
@@ -235,21 +240,19 @@ fa_bwd_dq_kernel(FaBwdParams p) {
 
   fa_f32x16 acc[NCB];  // dq^T: acc[cb] holds columns 32cb.., row qi
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-    asm volatile("" : "+a"(acc[cb]));  // placement only: the matrix core's AGPRs
-  }
 
-  load_block<D>(Kh, kv_lo * BB, N, loff, kbuf(0), wave);
-  load_block<D>(Vh, kv_lo * BB, N, loff, vbuf(0), wave);
+  load_block<D, BWQ>(Kh, kv_lo * BB, N, loff, kbuf(0), wave);
+  load_block<D, BWQ>(Vh, kv_lo * BB, N, loff, vbuf(0), wave);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   auto step = [&](int kt, int s) {
     if (kt + 1 < kv_hi) {
-      load_block<D>(Kh, (kt + 1) * BB, N, loff, kbuf(s ^ 1), wave);
-      load_block<D>(Vh, (kt + 1) * BB, N, loff, vbuf(s ^ 1), wave);
+      load_block<D, BWQ>(Kh, (kt + 1) * BB, N, loff, kbuf(s ^ 1), wave);
+      load_block<D, BWQ>(Vh, (kt + 1) * BB, N, loff, vbuf(s ^ 1), wave);
     }
     const int cls = fa_classify(qb0, qb1, kt * BB, BB, N, p.mask_kind, p.window);
     if (cls != FA_TILE_SKIP) {
@@ -365,8 +368,8 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
   // (one 4-byte load per lane by waves 0 and 1).  Rows past N read as zeros
   // and contribute nothing below, since their q and do rows are zero.
   auto load = [&](int qt, int b) {
-    load_block<D>(Qh, qt * BB, N, loff, qbuf(b), wave);
-    load_block<D>(dOh, qt * BB, N, loff, obuf(b), wave);
+    load_block<D, BW>(Qh, qt * BB, N, loff, qbuf(b), wave);
+    load_block<D, BW>(dOh, qt * BB, N, loff, obuf(b), wave);
     if (wave < 2) {
       const int r0 = qt * BB;
       const float* src = (wave == 0 ? lse_h : dl_h) + (r0 < N ? r0 : 0);
@@ -464,9 +467,10 @@ hipError_t launch_bwd(const FaBwdParams& p, hipStream_t stream) {
   const long long rows = (long long)p.BH * p.N;
   const unsigned dgrid = (unsigned)((rows + 256 / (D / 8) - 1) / (256 / (D / 8)));
   hipLaunchKernelGGL((fa_bwd_delta_kernel<DT, D>), dim3(dgrid), dim3(256), 0, stream, p);
-  const dim3 grid((unsigned)(p.BH * p.n_row_tiles));
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D>), grid, dim3(BW * 64), 0, stream, p);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D>), grid, dim3(BW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D>), dim3((unsigned)(p.BH * p.n_q_tiles)), dim3(BWQ * 64),
+                     0, stream, p);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D>), dim3((unsigned)(p.BH * p.n_k_tiles)), dim3(BW * 64),
+                     0, stream, p);
   return hipGetLastError();
 }
 

@@ -41,10 +41,12 @@ struct FaBwdParams {
   int window;
   float scale;
   float scale_log2;       // scale * log2(e), at least FLT_MIN
-  int n_row_tiles;        // ceil(N / (FA_BWD_WAVES * 32)): query tiles = key tiles
+  int n_q_tiles;          // ceil(N / (FA_BWD_DQ_WAVES * 32)): query tiles of the dq pass
+  int n_k_tiles;          // ceil(N / (FA_BWD_WAVES * 32)): key tiles of the dk/dv pass
   int heavy_first;        // 1: longest query tiles of the dq pass first (masks)
 };
-constexpr int FA_BWD_WAVES = 4;
+constexpr int FA_BWD_WAVES = 4;     // wavefronts per workgroup, dk/dv pass (one per SIMD)
+constexpr int FA_BWD_DQ_WAVES = 8;  // wavefronts per workgroup, dq pass (two per SIMD)
 
 // Decoding against a key/value cache (fa_decode.hip).
 struct FaDecodeParams {
