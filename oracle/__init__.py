@@ -23,6 +23,14 @@ heads share one key/value head (``kv_head``: consecutive groups).
 ``attention_decode`` evaluates a few queries at the last positions of a
 longer key/value cache (per (batch, head) through ``attention_rows``).
 
+``decode_e4m3`` gives the value of each OCP E4M3 code (the FP8 format of
+the FlashAttention-3 section of "FlashAttention (NL)" as gfx950 implements
+it), written out from the format's definition; ``attention_fp8`` is
+``attention_gqa`` on the decoded inputs, times the V factor: the exact
+attention of the values the codes stand for.  ``attention_weights_rows``
+returns the softmax weights of a few query rows (numpy, fp64), from which
+the tests build the error bound of a kernel that rounds the weights.
+
 ``attention_bwd`` / ``attention_bwd_rows`` / ``attention_bwd_keys`` call
 ``attn_bwd_oracle.c``: the gradients dq, dk, dv of the same definition for
 an output gradient do (chain rule written out, fp64).
@@ -281,6 +289,77 @@ def attention_bwd_keys(q, k, v, do, keys, scale: float, mask: str = "none",
     if rc != 0:
         raise RuntimeError("oracle_attn_bwd_keys_f64 failed (%d)" % rc)
     return dk, dv
+
+
+def _codes(x) -> np.ndarray:
+    """uint8 numpy array of the bytes of x (torch float8 / uint8 tensor or
+    numpy / list of ints 0..255)."""
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().to("cpu")
+        if x.dtype != torch.uint8:
+            x = x.view(torch.uint8)
+        return x.numpy()
+    a = np.asarray(x)
+    if a.dtype != np.uint8:
+        if np.any((a < 0) | (a > 255)):
+            raise ValueError("codes must lie in 0..255")
+        a = a.astype(np.uint8)
+    return a
+
+
+def decode_e4m3(codes) -> np.ndarray:
+    """fp64 values of OCP E4M3 codes: bit 7 sign, bits 6-3 exponent field e
+    (bias 7), bits 2-0 mantissa m.  e = 0: subnormal, m 2^-9 (2^(1-7) m/8);
+    otherwise (1 + m/8) 2^(e-7); e = 15 with m = 7 is NaN (the format has no
+    infinities, so its largest finite value is 1.75 x 2^8 = 448)."""
+    c = _codes(codes).astype(np.int64)
+    sign = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag)
+
+
+def attention_fp8(q8, k8, v8, scale: float, v_scale: float = 1.0, mask: str = "none",
+                  window: int = 0):
+    """o, lse (fp64) for E4M3 codes q8 [B, H, N, d], k8, v8 [B, H_kv, N, d]:
+    every code taken at its value (``decode_e4m3``), attention as in
+    ``attention_gqa``, o multiplied by v_scale.  Codes that are NaN are
+    refused."""
+    q, k, v = (decode_e4m3(x) for x in (q8, k8, v8))
+    if np.isnan(q).any() or np.isnan(k).any() or np.isnan(v).any():
+        raise ValueError("NaN codes in the inputs")
+    o, lse = attention_gqa(q, k, v, scale, mask, window)
+    return o * float(v_scale), lse
+
+
+def attention_weights_rows(q_rows, pos, k, scale: float, mask: str = "none",
+                           window: int = 0) -> np.ndarray:
+    """Softmax weights W[R, N] (fp64) of query vectors q_rows[R, d] at
+    positions pos[R] over the keys k[N, d] of one slice: W_rj = exp(s_rj) /
+    sum_j exp(s_rj) over visible j with s = scale q k^T, 0 where j is not
+    visible (a row that sees nothing is all 0).  Computed with numpy, max
+    subtracted before the exponential."""
+    q_rows, k = _f64(q_rows), _f64(k)
+    pos = np.asarray(pos, dtype=np.int64)
+    R, N = q_rows.shape[0], k.shape[0]
+    s = float(scale) * (q_rows @ k.T)
+    j = np.arange(N)[None, :]
+    i = pos[:, None]
+    if mask == "none":
+        vis = np.ones((R, N), dtype=bool)
+    elif mask == "causal":
+        vis = j <= i
+    else:
+        vis = (j <= i) & (j > i - int(window))
+    s = np.where(vis, s, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    mx = np.where(np.isfinite(mx), mx, 0.0)
+    w = np.where(vis, np.exp(s - mx), 0.0)
+    z = w.sum(axis=1, keepdims=True)
+    return np.where(z > 0, w / np.where(z > 0, z, 1.0), 0.0)
 
 
 def visible(i: int, j: int, mask: str, window: int) -> bool:
