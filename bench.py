@@ -21,7 +21,8 @@ Prints ONE JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        (NAME: one of seeded_inputs.BY_NAME, which includes the long-context
-       shape with shared key/value heads, fa_fwd_gqa)
+       shape with shared key/value heads, fa_fwd_gqa, and the E4M3 shapes,
+       fa_fwd_fp8, timed against the 5033.2 TFLOP/s dense E4M3 peak)
        [--no-cpu-baseline] [--copy-calibration]
        python bench.py --n-sweep   (traffic-vs-N evidence, bf16 causal B=1 H=32 d=128)
        python bench.py --bwd       (backward pass, B=1 H=32 N=16384 d=128 bf16 causal)
@@ -42,9 +43,11 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "e4m3": 5033.2}
 METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak (bf16 causal, N=16384, d=128)"
-KERNEL_SOURCES = ["exact_io_aware_04_amd/csrc/fa_fwd.hip", "exact_io_aware_04_amd/csrc/fa_device.h",
+METRIC_FP8 = "attention fwd TFLOP/s + % E4M3 MFMA peak (e4m3 causal, N=16384, d=128)"
+KERNEL_SOURCES = ["exact_io_aware_04_amd/csrc/fa_fwd.hip", "exact_io_aware_04_amd/csrc/fa_fwd8.hip",
+                  "exact_io_aware_04_amd/csrc/fa_fwd_common.h", "exact_io_aware_04_amd/csrc/fa_device.h",
                   "exact_io_aware_04_amd/csrc/fa_kernels.h", "exact_io_aware_04_amd/csrc/tile_class.h",
                   "exact_io_aware_04_amd/csrc/fa_api.cpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.json")
@@ -132,12 +135,13 @@ def step_flops(w) -> float:
 
 
 def algorithmic_bytes(w) -> int:
-    """Q, K, V read once, O written once (input dtype), lse written (fp32);
-    K and V have kv_heads heads."""
-    esz = 4 if w.dtype == "f32" else 2
+    """Q, K, V read once, O written once (input dtype; bf16 for E4M3
+    inputs), lse written (fp32); K and V have kv_heads heads."""
+    esz = {"f32": 4, "e4m3": 1}.get(w.dtype, 2)
+    osz = 2 if w.dtype == "e4m3" else esz
     n = w.B * w.H * w.N
     n_kv = w.B * w.kv_heads * w.N
-    return (2 * n + 2 * n_kv) * w.d * esz + 4 * n
+    return (n + 2 * n_kv) * w.d * esz + n * w.d * osz + 4 * n
 
 
 def load_traffic(w):
@@ -154,6 +158,11 @@ def load_traffic(w):
     if not ent:
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+def torch_index(rows):
+    import torch
+    return torch.from_numpy(rows)
 
 
 def cpu_baseline(w, q, k, v, target_s: float = 12.0):
@@ -179,6 +188,12 @@ def cpu_baseline(w, q, k, v, target_s: float = 12.0):
 
     def run(bh, rows):
         b, h = heads[bh]
+        if w.dtype == "e4m3":  # the oracle decodes the codes first (timed)
+            t0 = time.perf_counter()
+            qq = oracle.decode_e4m3(q[b, h][torch_index(rows)])
+            kk, vv = (oracle.decode_e4m3(t[b, h // group]) for t in (k, v))
+            oracle.attention_rows(qq, rows, kk, vv, w.scale, w.mask, w.window)
+            return time.perf_counter() - t0
         qq = q[b, h].double().numpy()
         kk, vv = (t[b, h // group].double().numpy() for t in (k, v))
         t0 = time.perf_counter()
@@ -527,18 +542,25 @@ def main():
 
     q, k, v = si.make_workload(w)
     dev = "cuda:0"
+    fp8 = w.dtype == "e4m3"
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    o = torch.empty_like(qd)
+    o = torch.empty(qd.shape, dtype=torch.bfloat16 if fp8 else qd.dtype, device=dev)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    dcode = {"f32": fa.FA_DTYPE_F32, "f16": fa.FA_DTYPE_F16, "bf16": fa.FA_DTYPE_BF16}[w.dtype]
     ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr())
-    rest = (w.N, w.d, float(w.scale), fa.MASKS[w.mask], int(w.window), dcode, dcode,
-            stream.cuda_stream)
-    if w.kv_heads == w.H:
-        entry, call = fa.fa_fwd, ptrs + (w.B, w.H) + rest
+    if fp8:
+        # E4M3 inputs, bf16 output, V factor 1
+        entry = fa.fa_fwd_fp8
+        call = ptrs + (w.B, w.H, w.kv_heads, w.N, w.d, float(w.scale), 1.0, fa.MASKS[w.mask],
+                       int(w.window), fa.FA_DTYPE_BF16, stream.cuda_stream)
     else:
-        entry, call = fa.fa_fwd_gqa, ptrs + (w.B, w.H, w.kv_heads) + rest
+        dcode = {"f32": fa.FA_DTYPE_F32, "f16": fa.FA_DTYPE_F16, "bf16": fa.FA_DTYPE_BF16}[w.dtype]
+        rest = (w.N, w.d, float(w.scale), fa.MASKS[w.mask], int(w.window), dcode, dcode,
+                stream.cuda_stream)
+        if w.kv_heads == w.H:
+            entry, call = fa.fa_fwd, ptrs + (w.B, w.H) + rest
+        else:
+            entry, call = fa.fa_fwd_gqa, ptrs + (w.B, w.H, w.kv_heads) + rest
 
     def step():
         st = entry(*call)
@@ -570,7 +592,7 @@ def main():
     achieved = flops / (avg_kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     res = {
-        "metric": METRIC,
+        "metric": METRIC_FP8 if fp8 else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -581,7 +603,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) Q/K/V, seed %d)" % w.seed,
+        "data": "synthetic (seeded N(0,1) Q/K/V%s, seed %d)" % (
+            " cast to E4M3, bf16 output" if fp8 else "", w.seed),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "N": w.N, "d": w.d,
                    "mask": w.mask, "window": w.window, "scale": w.scale,
                    "flops_per_step": flops, "pct_of_peak": round(100 * value / peak, 2)},
@@ -592,7 +615,7 @@ def main():
                      "kernel_min_ms": round(min(kern_ms), 4),
                      "algorithmic_bytes": algorithmic_bytes(w)},
     }
-    if w.dtype != "f32":
+    if w.dtype in ("bf16", "f16"):
         ceil = mfma_ceiling(torch, fa)
         res["roofline"]["measured_ceiling"] = ceil
         res["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceil["tflops"], 4)

@@ -1,7 +1,7 @@
 """Python binding of libfa.so: the fused exact attention forward pass on
 gfx950 (MI355X).
 
-The functions named like the C ABI (``fa_fwd``, ``fa_fwd_gqa``, ``fa_decode``,
+The functions named like the C ABI (``fa_fwd``, ``fa_fwd_gqa``, ``fa_fwd_fp8``, ``fa_decode``,
 ``fa_decode_workspace_bytes``, ``fa_bwd``, ``fa_fwd_record_tiles``,
 ``fa_tile_shape``, ``fa_tile_map``, ``fa_status_string``, ``fa_last_error``,
 ``fa_probe_mfma``, ``fa_mfma_ceiling``) only marshal arguments: pointers are plain integers
@@ -9,7 +9,8 @@ The functions named like the C ABI (``fa_fwd``, ``fa_fwd_gqa``, ``fa_decode``,
 handle (``torch.cuda.current_stream().cuda_stream``), and every step of the
 computation runs in the library's kernels.  ``attention`` is the torch-facing
 convenience: it allocates o and lse with torch on the inputs' device and
-calls ``fa_fwd`` on the current stream.
+calls ``fa_fwd`` on the current stream; ``attention_fp8``, ``attention_bwd``
+and ``attention_decode`` do the same for the other entry points.
 
 There is no fallback: if libfa.so is not built, loading fails loudly.
 """
@@ -24,7 +25,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfa.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "fa.h")
 
-FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
+FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16, FA_DTYPE_E4M3 = 0, 1, 2, 3
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_SLIDING = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_NO_DEVICE, FA_ERR_HIP = range(5)
 FA_TILE_SKIP, FA_TILE_FULL, FA_TILE_PARTIAL = 0, 1, 2
@@ -55,6 +56,8 @@ def load():
     lib.fa_fwd.restype = i
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp]
     lib.fa_fwd_gqa.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, i, i, i, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, i, i, vp]
     lib.fa_bwd.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -97,6 +100,12 @@ def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, mask_kind, window, in_d
                out_dtype, stream) -> int:
     return load().fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, mask_kind, window,
                              in_dtype, out_dtype, stream)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, H, H_kv, N, d, scale, v_scale, mask_kind, window,
+               out_dtype, stream) -> int:
+    return load().fa_fwd_fp8(q, k, v, o, lse, B, H, H_kv, N, d, scale, v_scale, mask_kind,
+                             window, out_dtype, stream)
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, mask_kind, window,
@@ -214,6 +223,44 @@ def attention(q, k, v, scale=None, mask: str = "none", window: int = 0,
             st = fa_fwd(*ptrs, B, H, *rest, stream)
     if st != FA_OK:
         raise FaError(st, "fa_fwd")
+    return o, lse
+
+
+def attention_fp8(q, k, v, scale=None, v_scale: float = 1.0, mask: str = "none",
+                  window: int = 0, out_dtype=None):
+    """o, lse of attention for E4M3 device tensors (torch.float8_e4m3fn, or
+    uint8 holding E4M3 codes) q [B, H, N, d] and k, v [B, H_kv, N, d]:
+    o = v_scale softmax(scale q k^T + mask) v with every code taken at its
+    value (``fa_fwd_fp8``).  ``out_dtype``: torch.bfloat16 (default),
+    torch.float16 or torch.float32; lse is float32 [B, H, N]."""
+    import torch
+    allowed = (torch.float8_e4m3fn, torch.uint8)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, H, N, d] and k, v [B, H_kv, N, d]")
+    if (k.shape[0], k.shape[2], k.shape[3]) != (q.shape[0], q.shape[2], q.shape[3]):
+        raise ValueError("k, v must match q in B, N and d")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if not all(t.dtype in allowed for t in (q, k, v)):
+        raise ValueError("q, k, v must be float8_e4m3fn (or uint8 E4M3 codes)")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if H_kv < 1 or H % H_kv:
+        raise ValueError("the key/value head count %d must divide H = %d" % (H_kv, H))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    o = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        B, H, H_kv, N, d, float(scale), float(v_scale), MASKS[mask], int(window),
+                        _dtype_code(out_dtype), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
     return o, lse
 
 

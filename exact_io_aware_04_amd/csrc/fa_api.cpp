@@ -37,7 +37,9 @@ int ok() {
   return FA_OK;
 }
 
-size_t elem_bytes(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
+size_t elem_bytes(int dtype) {
+  return dtype == FA_DTYPE_F32 ? 4 : dtype == FA_DTYPE_E4M3 ? 1 : 2;
+}
 
 bool valid_dtype(int t) {
   return t == FA_DTYPE_F32 || t == FA_DTYPE_F16 || t == FA_DTYPE_BF16;
@@ -61,9 +63,11 @@ int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
   if (H_kv < 1 || H_kv > H || H % H_kv != 0)
     return fail(FA_ERR_INVALID_ARG, "H_kv must divide H = %d (got %d)", H, H_kv);
   if (N >= (1 << 30)) return fail(FA_ERR_INVALID_ARG, "N must be < 2^30 (got %d)", N);
-  if (!valid_dtype(in_dtype)) return fail(FA_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
+  const bool e4m3 = in_dtype == FA_DTYPE_E4M3;
+  if (!valid_dtype(in_dtype) && !e4m3)
+    return fail(FA_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
   if (!valid_dtype(out_dtype)) return fail(FA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
-  if (out_dtype != in_dtype && out_dtype != FA_DTYPE_F32)
+  if (!e4m3 && out_dtype != in_dtype && out_dtype != FA_DTYPE_F32)
     return fail(FA_ERR_INVALID_ARG, "out_dtype must equal in_dtype or be F32");
   if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL && mask_kind != FA_MASK_SLIDING)
     return fail(FA_ERR_INVALID_ARG, "unknown mask_kind %d", mask_kind);
@@ -80,7 +84,8 @@ int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
   const long long tiles = bh * ((N + rows_wg - 1) / rows_wg);
   if (tiles > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "too many row tiles for one grid");
   if (!fa_head_dim_built(in_dtype, d))
-    return fail(FA_ERR_UNSUPPORTED, "head dim %d not built (64, 128; 256 for f16/bf16)", d);
+    return fail(FA_ERR_UNSUPPORTED, e4m3 ? "E4M3 head dim %d not built (128)"
+                                         : "head dim %d not built (64, 128; 256 for f16/bf16)", d);
   const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u;
   if (mis) return fail(FA_ERR_INVALID_ARG, "q, k, v, o must be 16-byte aligned");
   if (((uintptr_t)lse & 3u) != 0) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
@@ -122,8 +127,8 @@ int check_device() {
 }
 
 int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-            int H, int H_kv, int N, int d, float scale, int mask_kind, int window,
-            int in_dtype, int out_dtype, unsigned char* tiles, void* stream) {
+            int H, int H_kv, int N, int d, float scale, float v_scale, int mask_kind,
+            int window, int in_dtype, int out_dtype, unsigned char* tiles, void* stream) {
   int st = check_args(q, k, v, o, lse, B, H, H_kv, N, d, scale, mask_kind, window,
                       in_dtype, out_dtype);
   if (st != FA_OK) return st;
@@ -149,10 +154,13 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   // is 1 to fp32 precision -- the uniform weights scale = 0 defines.
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   if (!(p.scale_log2 >= FLT_MIN)) p.scale_log2 = FLT_MIN;
+  p.v_scale = v_scale;
   p.n_row_tiles = (N + fa_rows_per_wg(in_dtype, d) - 1) / fa_rows_per_wg(in_dtype, d);
   p.xcd_split = (p.BH % 8 == 0) ? 1 : 0;
   p.heavy_first = mask_kind != FA_MASK_NONE ? 1 : 0;
-  hipError_t e = fa_launch_fwd(in_dtype, out_dtype, d, p, (hipStream_t)stream);
+  hipError_t e = in_dtype == FA_DTYPE_E4M3
+                     ? fa_launch_fwd8(out_dtype, d, p, (hipStream_t)stream)
+                     : fa_launch_fwd(in_dtype, out_dtype, d, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -378,22 +386,37 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
            int N, int d, float scale, int mask_kind, int window, int in_dtype, int out_dtype,
            void* stream) {
-  return run_fwd(q, k, v, o, lse, B, H, H, N, d, scale, mask_kind, window, in_dtype,
+  if (in_dtype == FA_DTYPE_E4M3)
+    return fail(FA_ERR_INVALID_ARG, "E4M3 inputs go through fa_fwd_fp8");
+  return run_fwd(q, k, v, o, lse, B, H, H, N, d, scale, 1.f, mask_kind, window, in_dtype,
                  out_dtype, nullptr, stream);
 }
 
 int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                int H, int H_kv, int N, int d, float scale, int mask_kind, int window,
                int in_dtype, int out_dtype, void* stream) {
-  return run_fwd(q, k, v, o, lse, B, H, H_kv, N, d, scale, mask_kind, window, in_dtype,
+  if (in_dtype == FA_DTYPE_E4M3)
+    return fail(FA_ERR_INVALID_ARG, "E4M3 inputs go through fa_fwd_fp8");
+  return run_fwd(q, k, v, o, lse, B, H, H_kv, N, d, scale, 1.f, mask_kind, window, in_dtype,
                  out_dtype, nullptr, stream);
+}
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+               int H, int H_kv, int N, int d, float scale, float v_scale, int mask_kind,
+               int window, int out_dtype, void* stream) {
+  if (!std::isfinite(v_scale))
+    return fail(FA_ERR_INVALID_ARG, "v_scale must be finite");
+  return run_fwd(q, k, v, o, lse, B, H, H_kv, N, d, scale, v_scale, mask_kind, window,
+                 FA_DTYPE_E4M3, out_dtype, nullptr, stream);
 }
 
 int fa_fwd_record_tiles(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int H, int N, int d, float scale, int mask_kind, int window,
                         int in_dtype, int out_dtype, unsigned char* tiles, void* stream) {
   if (!tiles) return fail(FA_ERR_INVALID_ARG, "null tiles buffer");
-  return run_fwd(q, k, v, o, lse, B, H, H, N, d, scale, mask_kind, window, in_dtype,
+  if (in_dtype == FA_DTYPE_E4M3)
+    return fail(FA_ERR_INVALID_ARG, "E4M3 inputs go through fa_fwd_fp8");
+  return run_fwd(q, k, v, o, lse, B, H, H, N, d, scale, 1.f, mask_kind, window, in_dtype,
                  out_dtype, tiles, stream);
 }
 
@@ -447,13 +470,14 @@ const char* fa_status_string(int status) {
 const char* fa_last_error(void) { return g_last_error.c_str(); }
 
 int fa_probe_mfma(int which, const void* a, const void* b, float* d, void* stream) {
-  if (which < 0 || which > 2) return fail(FA_ERR_INVALID_ARG, "which must be 0, 1 or 2");
+  if (which < 0 || which > 4) return fail(FA_ERR_INVALID_ARG, "which must be 0 .. 4");
   if (!a || !b || !d) return fail(FA_ERR_INVALID_ARG, "null pointer argument");
   if ((((uintptr_t)a | (uintptr_t)b) & 15u) != 0 || ((uintptr_t)d & 3u) != 0)
     return fail(FA_ERR_INVALID_ARG, "misaligned operand");
   int st = check_device();
   if (st != FA_OK) return st;
-  hipError_t e = fa_launch_probe(which, a, b, d, (hipStream_t)stream);
+  hipError_t e = which <= 2 ? fa_launch_probe(which, a, b, d, (hipStream_t)stream)
+                            : fa_launch_probe8(which - 3, a, b, d, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -62,6 +62,7 @@
 #include <hip/hip_runtime.h>
 
 #include "fa_device.h"
+#include "fa_fwd_common.h"
 #include "fa_kernels.h"
 #include "tile_class.h"
 
@@ -72,45 +73,6 @@ namespace {
 // ---------------------------------------------------------------------------
 // pieces shared by both kernels
 // ---------------------------------------------------------------------------
-
-// Work item of this workgroup: (batch*head, first query row).
-template <int ROWS_WG>
-__device__ __forceinline__ void work_item(const FaFwdParams& p, int& bh, int& q0) {
-  const int T = p.n_row_tiles;
-  const int b = blockIdx.x;
-  int rank;
-  if (p.xcd_split) {
-    const int hpx = p.BH >> 3;  // heads per XCD
-    const int s = b >> 3;
-    bh = (b & 7) * hpx + s % hpx;
-    rank = s / hpx;
-  } else {
-    bh = b % p.BH;
-    rank = b / p.BH;
-  }
-  const int qt = p.heavy_first ? (T - 1 - rank) : rank;
-  q0 = qt * ROWS_WG;
-}
-
-// Boundary blocks: scores of invisible keys become -inf, which the
-// exponential maps to exactly 0 (scale_log2 > 0).  s[kb][r] is the score of
-// key k0 + 32kb + 8(r/4) + 4half + r%4 for query qi.
-template <int NKB>
-__device__ __forceinline__ void apply_mask(fa_f32x16 (&s)[NKB], int k0, int qi, int half, int N,
-                                           int mask_kind, int window) {
-  // row qi sees keys jlo..jhi; key j is visible iff 0 <= j - jlo <= span
-  const int jhi = mask_kind == FA_MASKK_NONE ? N - 1 : min(qi, N - 1);
-  const int jlo = mask_kind == FA_MASKK_SLIDING ? max(qi - window + 1, 0) : 0;
-  const int base = k0 + 4 * half - jlo;
-  const unsigned int span = (unsigned int)(jhi - jlo);
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-      s[kb][r] = (unsigned int)(base + off) <= span ? s[kb][r] : FA_NEG_INF;
-    }
-}
 
 // Online-softmax step on one key block: row maximum, reference update with
 // O rescale (rare), probabilities p = 2^(s*scale*log2e - m).

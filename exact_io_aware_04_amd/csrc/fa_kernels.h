@@ -1,5 +1,6 @@
 // Internal interface between the host API (fa_api.cpp) and the gfx950
-// kernels (fa_fwd.hip).  Not part of the public ABI.
+// kernels (fa_fwd.hip, fa_fwd8.hip, fa_bwd.hip, fa_decode.hip).  Not part
+// of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,6 +19,7 @@ struct FaFwdParams {
   int mask_kind;          // FA_MASKK_*
   int window;             // sliding window (keys), >= 1 when sliding
   float scale_log2;       // scale * log2(e)
+  float v_scale;          // E4M3 inputs: factor applied to O (1 otherwise)
   int n_row_tiles;        // ceil(N / rows_per_workgroup)
   int xcd_split;          // 1: give each XCD its own heads (BH % 8 == 0)
   int heavy_first;        // 1: longest row tiles launched first (masks)
@@ -82,7 +84,11 @@ constexpr int FA_WAVES_16 = 8;           // wavefronts per workgroup, f16/bf16
 constexpr int FA_WAVES_WIDE = 4;         // wavefronts per workgroup, f16/bf16 at d = 256
 constexpr int FA_KEYS_16 = 64;           // keys per K/V block, f16/bf16
 constexpr int FA_KEYS_32 = 32;           // keys per K/V block, f32
+constexpr int FA_KEYS_8 = 64;            // keys per K/V block, E4M3
 constexpr int FA_STAGES_16 = 3;          // depth of the K and V rings in LDS, f16/bf16
+
+// Input dtype codes: 0 f32, 1 f16, 2 bf16 (as in fa.h), 3 E4M3 (fa_fwd_fp8).
+constexpr int FA_DT_E4M3 = 3;
 
 // keys per K/V block for an input dtype code (0 = f32) and head dim
 constexpr int fa_keys_per_block(int in_dtype, int d) {
@@ -94,14 +100,19 @@ constexpr int fa_rows_per_wg(int in_dtype, int d) {
   return (in_dtype == 0 ? FA_WAVES_32 : d == 256 ? FA_WAVES_WIDE : FA_WAVES_16) * FA_ROW_BLOCK;
 }
 
-// head dims built for an input dtype code: 64 and 128, and 256 for f16/bf16
+// head dims built for an input dtype code: 64 and 128, 256 for f16/bf16,
+// 128 only for E4M3
 constexpr bool fa_head_dim_built(int in_dtype, int d) {
+  if (in_dtype == FA_DT_E4M3) return d == 128;
   return d == 64 || d == 128 || (d == 256 && in_dtype != 0);
 }
 
 // dtype codes as in fa.h
 hipError_t fa_launch_fwd(int in_dtype, int out_dtype, int d,
                          const FaFwdParams& p, hipStream_t stream);
+hipError_t fa_launch_fwd8(int out_dtype, int d, const FaFwdParams& p, hipStream_t stream);
+hipError_t fa_launch_probe8(int which, const void* a, const void* b, float* d,
+                            hipStream_t stream);
 hipError_t fa_launch_bwd(int in_dtype, int d, const FaBwdParams& p, hipStream_t stream);
 hipError_t fa_launch_decode(int in_dtype, int d, const FaDecodeParams& p, hipStream_t stream);
 hipError_t fa_launch_probe(int which, const void* a, const void* b, float* d,

@@ -55,7 +55,8 @@
 extern "C" {
 #endif
 
-enum { FA_DTYPE_F32 = 0, FA_DTYPE_F16 = 1, FA_DTYPE_BF16 = 2 };
+enum { FA_DTYPE_F32 = 0, FA_DTYPE_F16 = 1, FA_DTYPE_BF16 = 2,
+       FA_DTYPE_E4M3 = 3 /* 8-bit float inputs of fa_fwd_fp8 only */ };
 enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_SLIDING = 2 };
 enum {
   FA_OK = 0,
@@ -107,6 +108,40 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int H_kv, int N, int d, float scale, int mask_kind,
                int window, int in_dtype, int out_dtype, void* stream);
+
+/*
+ * Forward pass with 8-bit floating-point inputs: the FP8 precision that
+ * "FlashAttention (NL)", section "FlashAttention-3 (2024)", names for the
+ * Hopper version.  q, k, v hold OCP E4M3 codes (1 sign bit, 4 exponent bits
+ * with bias 7, 3 mantissa bits; exponent field 0 is subnormal, m 2^-9;
+ * S.1111.111 is NaN; no infinities; largest finite 448), the format of
+ * gfx950's 8-bit matrix instructions and of torch.float8_e4m3fn.  With
+ * x(c) the value of code c:
+ *
+ *   s_ij = scale * <x(q[b,h,i,:]), x(k[b,h/g,j,:])>     for visible j
+ *   o[b,h,i] = v_scale * sum_j exp(s_ij) x(v[b,h/g,j,:]) / sum_j exp(s_ij)
+ *   lse[b,h,i] = ln sum_j exp(s_ij)
+ *
+ * so per-tensor dequantisation factors fold into the call: scale = softmax
+ * scale * q factor * k factor, v_scale = v factor.
+ *   q [B][H][N][d], k, v [B][H_kv][N][d]: E4M3 bytes, no NaN codes
+ *   o [B][H][N][d] of out_dtype (F32, F16 or BF16); lse [B][H][N] float
+ *   d = 128 (else FA_ERR_UNSUPPORTED); v_scale finite (else
+ *   FA_ERR_INVALID_ARG); H_kv, masks, scale, alignment, stream, ownership
+ *   and errors as in fa_fwd_gqa.
+ * Arithmetic: both products on the E4M3 matrix instructions with fp32
+ * accumulation (the hardware sums the 64 products of one instruction to
+ * about 2^-12 of the largest of them); softmax statistics in fp32; the
+ * probabilities, scaled by 2^3 relative to the running reference, are rounded
+ * to E4M3 (nearest even) before the product with V, and O is divided by the
+ * fp32 sum of the unrounded ones.  Each weight therefore carries a relative
+ * error up to 2^-4 (normal range), or an absolute one up to 2^-13 of the
+ * largest weight of its row (subnormal range); lse is not affected by that
+ * rounding.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int H_kv, int N, int d, float scale, float v_scale,
+               int mask_kind, int window, int out_dtype, void* stream);
 
 /*
  * Decoding against a key/value cache: Nq queries per head at the last Nq
@@ -210,10 +245,14 @@ const char* fa_last_error(void);
 /*
  * Diagnostic: one 32x32 output block of a matrix-core product, to check the
  * operand and accumulator lane layouts the kernels rely on.  which = 0:
- * bf16 32x32x16; 1: f16 32x32x16; 2: f32 32x32x2.  a and b are device
- * pointers to 64 lanes x (8 for which 0/1, 1 for which 2) elements in lane
- * order, d a device pointer to 64 lanes x 16 floats in lane order.  The
- * kernel is launched on `stream` with one wavefront.
+ * bf16 32x32x16; 1: f16 32x32x16; 2: f32 32x32x2; 3: E4M3 32x32x64.  a and
+ * b are device pointers to 64 lanes x (8 for which 0/1, 1 for which 2, 32
+ * bytes for which 3) elements in lane order, d a device pointer to 64 lanes
+ * x 16 floats in lane order.  which = 4 checks the transposing LDS byte
+ * read instead: a holds 512 bytes, lane l addresses byte 8l, and d receives
+ * the 8 bytes each lane gets back (64 lanes x 8 floats; b must be non-null
+ * and is not read).  The kernel is launched on `stream` with one
+ * wavefront.
  */
 int fa_probe_mfma(int which, const void* a, const void* b, float* d,
                   void* stream);

@@ -28,7 +28,7 @@ def call(**kw):
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fa.load()
     names = fa.declared_functions()
-    assert {"fa_fwd", "fa_fwd_gqa", "fa_bwd", "fa_decode", "fa_decode_workspace_bytes", "fa_fwd_record_tiles", "fa_tile_shape", "fa_tile_map",
+    assert {"fa_fwd", "fa_fwd_gqa", "fa_fwd_fp8", "fa_bwd", "fa_decode", "fa_decode_workspace_bytes", "fa_fwd_record_tiles", "fa_tile_shape", "fa_tile_map",
             "fa_status_string", "fa_last_error", "fa_probe_mfma", "fa_mfma_ceiling"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -107,7 +107,8 @@ def test_record_tiles_needs_a_buffer():
 
 
 def test_probe_rejects_bad_arguments():
-    assert fa.fa_probe_mfma(3, Q, K, O, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_probe_mfma(5, Q, K, O, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_probe_mfma(-1, Q, K, O, None) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_probe_mfma(0, 0, K, O, None) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_probe_mfma(0, Q + 4, K, O, None) == fa.FA_ERR_INVALID_ARG
 
@@ -266,3 +267,65 @@ def test_decode_valid_arguments_reach_the_device_check():
     assert call_decode() in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
     assert call_decode(mask_kind=fa.FA_MASK_SLIDING, window=64, Nq=4, H=8, H_kv=1) in (
         fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
+
+
+# ---- 8-bit inputs (fa_fwd_fp8) ------------------------------------------------
+def call_fp8(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=8, H_kv=2, N=100, d=128, scale=0.1,
+                v_scale=1.0, mask_kind=fa.FA_MASK_CAUSAL, window=0,
+                out_dtype=fa.FA_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_fp8(*(args[n] for n in ("q", "k", "v", "o", "lse", "B", "H", "H_kv", "N",
+                                             "d", "scale", "v_scale", "mask_kind", "window",
+                                             "out_dtype", "stream")))
+
+
+@pytest.mark.parametrize("kw", [dict(q=0), dict(lse=0), dict(B=0), dict(N=0), dict(H_kv=3),
+                                dict(v_scale=float("inf")), dict(v_scale=float("nan")),
+                                dict(scale=-1.0), dict(out_dtype=3), dict(out_dtype=7),
+                                dict(mask_kind=fa.FA_MASK_SLIDING, window=0),
+                                dict(q=Q + 8), dict(o=Q + 64)], ids=str)
+def test_fp8_invalid_arguments_are_rejected_on_the_host(kw):
+    assert call_fp8(**kw) == fa.FA_ERR_INVALID_ARG, fa.fa_last_error()
+
+
+@pytest.mark.parametrize("d", [64, 256, 96])
+def test_fp8_head_dims_other_than_128_are_unsupported(d):
+    assert call_fp8(d=d) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_fp8_codes_are_refused_by_the_16_bit_entry_points():
+    assert call(in_dtype=fa.FA_DTYPE_E4M3, out_dtype=fa.FA_DTYPE_BF16) == fa.FA_ERR_INVALID_ARG
+    assert call_gqa(in_dtype=fa.FA_DTYPE_E4M3) == fa.FA_ERR_INVALID_ARG
+    st = fa.fa_fwd_record_tiles(Q, K, V, O, L, 1, 1, 100, 128, 0.1, 1, 0, fa.FA_DTYPE_E4M3,
+                                fa.FA_DTYPE_BF16, 4 * A, None)
+    assert st == fa.FA_ERR_INVALID_ARG
+
+
+def test_fp8_overlap_checks_use_one_byte_elements():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    # k holds B*H_kv*N*d E4M3 codes = 2 * 100 * 128 bytes
+    kbytes = 2 * 100 * 128
+    assert call_fp8(o=K + kbytes) in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP), fa.fa_last_error()
+    assert call_fp8(o=K + kbytes - 16) == fa.FA_ERR_INVALID_ARG
+
+
+def test_fp8_valid_arguments_reach_the_device_check():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    for out in (fa.FA_DTYPE_F32, fa.FA_DTYPE_F16, fa.FA_DTYPE_BF16):
+        assert call_fp8(out_dtype=out) in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
+    assert call_fp8(H_kv=8, mask_kind=fa.FA_MASK_SLIDING, window=5, v_scale=-0.5) in (
+        fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
+
+
+def test_fp8_torch_wrapper_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(1, 2, 8, 128, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        fa.attention_fp8(q, q, q)          # host tensors
+    with pytest.raises(ValueError):
+        fa.attention_fp8(q.float(), q, q)  # not E4M3
