@@ -11,8 +11,9 @@
 // v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32), twice the rate of the
 // 16-bit products.
 //
-// Work decomposition, K/V rings, ping-pong of the two wavefronts of a SIMD,
-// tile classes and work order are those of fa_fwd16_kernel (fa_fwd.hip).
+// Work decomposition, ping-pong of the two wavefronts of a SIMD, tile
+// classes and work order are those of fa_fwd16_kernel (fa_fwd.hip); the K/V
+// rings have four slots (8 KB blocks).
 // What differs:
 //  * S^T = K Q^T contracts 64 head-dim elements per product.  Lane (row
 //    l32, half h) of both operands holds elements 64s + 32h .. 64s + 32h + 31
@@ -174,7 +175,9 @@ __device__ __forceinline__ void store_output8(const FaFwdParams& p, const fa_f32
 }
 
 // Eight wavefronts, 32 query rows each, two per SIMD, half a key block apart
-// (see fa_fwd16_kernel for the schedule and the ring discipline).
+// (see fa_fwd16_kernel for the schedule and the ring discipline; here the
+// rings have four slots, so K(kt+3) and V(kt+3) are loaded while block kt is
+// computed).
 template <int D, int OUT_DT>
 __global__ void __launch_bounds__(FA_WAVES_16 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd8_kernel(FaFwdParams p) {
@@ -191,11 +194,12 @@ fa_fwd8_kernel(FaFwdParams p) {
   static_assert(D == 128 && NKB == 2, "128-byte rows and 64-key blocks below");
   static_assert(LPW * NL * 1024 == TILEB, "loads must cover the block");
   static_assert(NL * 1024 / ROWB % 16 == 0, "pieces must be a multiple of 16 rows apart");
-  static_assert(NW == 8 && FA_STAGES_16 == 3, "schedule below: 2 x 4 wavefronts, rings of 3");
-  __shared__ __attribute__((aligned(1024))) unsigned char ks0[TILEB], ks1[TILEB], ks2[TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char vs0[TILEB], vs1[TILEB], vs2[TILEB];
-  auto kbuf = [&](int b) { return (FA_AS3 unsigned char*)(b == 0 ? ks0 : b == 1 ? ks1 : ks2); };
-  auto vbuf = [&](int b) { return (FA_AS3 unsigned char*)(b == 0 ? vs0 : b == 1 ? vs1 : vs2); };
+  constexpr int NSL = 4;  // ring slots: blocks are prefetched three steps ahead
+  static_assert(NW == 8, "schedule below: 2 x 4 wavefronts");
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[TILEB], ks1[TILEB], ks2[TILEB], ks3[TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs0[TILEB], vs1[TILEB], vs2[TILEB], vs3[TILEB];
+  auto kbuf = [&](int b) { return (FA_AS3 unsigned char*)(b == 0 ? ks0 : b == 1 ? ks1 : b == 2 ? ks2 : ks3); };
+  auto vbuf = [&](int b) { return (FA_AS3 unsigned char*)(b == 0 ? vs0 : b == 1 ? vs1 : b == 2 ? vs2 : vs3); };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -312,6 +316,7 @@ fa_fwd8_kernel(FaFwdParams p) {
     }
     float pr[NKB][16];
     float psum = 0.f;
+    float ps4[4];  // four independent partial sums (short dependency chains)
     bool exact = cls == FA_TILE_PARTIAL || __ballot(m_ref == FA_NEG_INF);
     if (!exact) {
 #pragma unroll
@@ -319,8 +324,9 @@ fa_fwd8_kernel(FaFwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           pr[kb][r] = exp2_hw(sc[kb][r] * c2);
-          psum += pr[kb][r];
+          ps4[r & 3] = kb == 0 && r < 4 ? pr[kb][r] : ps4[r & 3] + pr[kb][r];
         }
+      psum = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
       exact = __ballot(!(psum <= 256.f));
     }
     if (exact) {
@@ -348,8 +354,9 @@ fa_fwd8_kernel(FaFwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           pr[kb][r] = exp2_hw(__builtin_fmaf(sc[kb][r], c2, shift));
-          psum += pr[kb][r];
+          ps4[r & 3] = kb == 0 && r < 4 ? pr[kb][r] : ps4[r & 3] + pr[kb][r];
         }
+      psum = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
       const float mn = m_ref == FA_NEG_INF ? 0.f : -(m_ref - FA8_SHIFT) * inv_c2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc0[r] = mn;
@@ -359,15 +366,18 @@ fa_fwd8_kernel(FaFwdParams p) {
   };
 
   auto issue_step = [&](int kt, int s) {
-    if (kt + 2 < kv_hi) {
+    if (kt + NSL - 1 < kv_hi) {
       if (lead)
-        issue(Kh, koff, kbuf((s + 2) % 3), kt + 2);
+        issue(Kh, koff, kbuf((s + NSL - 1) % NSL), kt + NSL - 1);
       else
-        issue(Vh, voff, vbuf((s + 2) % 3), kt + 2);
+        issue(Vh, voff, vbuf((s + NSL - 1) % NSL), kt + NSL - 1);
     }
   };
+  // block kt+1 must have landed; blocks kt+2 and kt+3 may stay in flight
   auto wait_step = [&](int kt) {
-    if (kt + 2 < kv_hi)
+    if (kt + 3 < kv_hi)
+      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(2 * LPW));
+    else if (kt + 2 < kv_hi)
       __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(LPW));
     else
       __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
@@ -380,7 +390,7 @@ fa_fwd8_kernel(FaFwdParams p) {
         p.tiles[((size_t)bh * n_row_blocks + qb0 / FA_ROW_BLOCK) * n_key_blocks + kt] =
             (unsigned char)(cls_cur + 1);
     }
-    phase_mfma(s, (s + 2) % 3);
+    phase_mfma(s, (s + NSL - 1) % NSL);
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
     barrier_nofence();
     phase_softmax(kt, cls_cur);
@@ -395,14 +405,16 @@ fa_fwd8_kernel(FaFwdParams p) {
   if (lead) {
     issue(Kh, koff, kbuf(0), kv_lo);
     if (kv_lo + 1 < kv_hi) issue(Kh, koff, kbuf(1), kv_lo + 1);
+    if (kv_lo + 2 < kv_hi) issue(Kh, koff, kbuf(2), kv_lo + 2);
   } else {
     issue(Vh, voff, vbuf(0), kv_lo);
     if (kv_lo + 1 < kv_hi) issue(Vh, voff, vbuf(1), kv_lo + 1);
+    if (kv_lo + 2 < kv_hi) issue(Vh, voff, vbuf(2), kv_lo + 2);
   }
   static_assert(TILEB % (NW * 64 * 16) == 0, "zero fill must cover the slot");
 #pragma unroll
   for (int i = 0; i < TILEB / (NW * 64 * 16); ++i)
-    *(FA_AS3 fa_u32x4*)(vbuf(2) + (i * NW * 64 + tid) * 16) = fa_u32x4{0u, 0u, 0u, 0u};
+    *(FA_AS3 fa_u32x4*)(vbuf(NSL - 1) + (i * NW * 64 + tid) * 16) = fa_u32x4{0u, 0u, 0u, 0u};
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (!lead) barrier_nofence();
@@ -412,6 +424,8 @@ fa_fwd8_kernel(FaFwdParams p) {
     step(kt, 1);
     if (++kt > kv_hi) break;
     step(kt, 2);
+    if (++kt > kv_hi) break;
+    step(kt, 3);
     if (++kt > kv_hi) break;
   }
   if (lead) barrier_nofence();
