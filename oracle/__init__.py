@@ -33,7 +33,9 @@ the tests build the error bound of a kernel that rounds the weights.
 
 ``attention_bwd`` / ``attention_bwd_rows`` / ``attention_bwd_keys`` call
 ``attn_bwd_oracle.c``: the gradients dq, dk, dv of the same definition for
-an output gradient do (chain rule written out, fp64).
+an output gradient do (chain rule written out, fp64); ``attention_bwd_gqa``
+applies it per query head when key/value heads are shared and sums dk, dv
+over each group.
 
 Visibility of key j to query i: ``none`` all j; ``causal`` j <= i;
 ``sliding`` i - window < j <= i.
@@ -251,6 +253,32 @@ def attention_bwd(q, k, v, do, scale: float, mask: str = "none", window: int = 0
                                          _ptr(dq), _ptr(dk), _ptr(dv))
     if rc != 0:
         raise RuntimeError("oracle_attn_bwd_f64 failed (%d)" % rc)
+    return dq, dk, dv
+
+
+def attention_bwd_gqa(q, k, v, do, scale: float, mask: str = "none", window: int = 0):
+    """dq [B, H, N, d] and dk, dv [B, H_kv, N, d] (fp64) when query head h
+    reads key/value head kv_head(h, H, H_kv): every query head's gradients
+    by ``attention_bwd`` against its key/value head, and a key/value head's
+    dk, dv the sum over the query heads that read it (the chain rule through
+    the shared operand)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape or do.shape != q.shape:
+        raise ValueError("q, do must be [B, H, N, d] and k, v [B, H_kv, N, d]")
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if k.shape[0] != B or k.shape[2:] != (N, d) or H_kv < 1 or H % H_kv:
+        raise ValueError("k, v must be [B, H_kv, N, d] with H_kv dividing H")
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head(h, H, H_kv)
+            dq[b, h], dk_h, dv_h = attention_bwd(q[b, h], k[b, g], v[b, g], do[b, h], scale,
+                                                 mask, window)
+            dk[b, g] += dk_h
+            dv[b, g] += dv_h
     return dq, dk, dv
 
 

@@ -218,3 +218,55 @@ def test_backward_mutant_is_caught(name, tmp_path, swap_bwd_oracle):
     assert text.count(old) == 1, "mutation site not unique: %s" % name
     oracle._bwd_lib = oracle.bind_bwd(_compile(tmp_path, text.replace(old, new), name))
     assert battery(), "mutant %s passed every pin" % name
+
+
+# ---- shared key/value heads ------------------------------------------------------
+def torch_grads_gqa(q, k, v, do, scale, mask, window):
+    Q, K, V = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    vis = torch.from_numpy(visible_matrix(q.shape[-2], mask, window))
+    o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=vis, scale=scale,
+                                                         enable_gqa=True)
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    return Q.grad.numpy(), K.grad.numpy(), V.grad.numpy()
+
+
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 3)])
+@pytest.mark.parametrize("H,H_kv", [(4, 1), (4, 2), (6, 3)])
+def test_shared_heads_match_torch_autograd_fp64(mask, window, H, H_kv):
+    B, N, d = 2, 29, 8
+    q, do = rand((B, H, N, d), 141), rand((B, H, N, d), 142)
+    k, v = rand((B, H_kv, N, d), 143), rand((B, H_kv, N, d), 144)
+    dq, dk, dv = oracle.attention_bwd_gqa(q, k, v, do, 0.35, mask, window)
+    tq, tk, tv = torch_grads_gqa(q, k, v, do, 0.35, mask, window)
+    np.testing.assert_allclose(dq, tq, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, tk, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, tv, rtol=0, atol=1e-12)
+
+
+def test_shared_heads_with_one_head_per_group_is_plain_backward():
+    q, k, v, do = (rand((2, 3, 20, 5), 151 + s) for s in range(4))
+    a = oracle.attention_bwd_gqa(q, k, v, do, 0.7, "causal")
+    b = oracle.attention_bwd(q, k, v, do, 0.7, "causal")
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_shared_heads_equal_copied_heads_summed():
+    # copying each key/value head to its g query heads and summing the
+    # copies' gradients gives the shared heads' gradients
+    B, H, H_kv, N, d = 1, 6, 2, 24, 4
+    q, do = rand((B, H, N, d), 161), rand((B, H, N, d), 162)
+    k, v = rand((B, H_kv, N, d), 163), rand((B, H_kv, N, d), 164)
+    g = H // H_kv
+    kc, vc = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+    dq, dk, dv = oracle.attention_bwd_gqa(q, k, v, do, 0.5, "sliding", 5)
+    cq, ck, cv = oracle.attention_bwd(q, kc, vc, do, 0.5, "sliding", 5)
+    np.testing.assert_array_equal(dq, cq)
+    np.testing.assert_allclose(dk, ck.reshape(B, H_kv, g, N, d).sum(axis=2), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(dv, cv.reshape(B, H_kv, g, N, d).sum(axis=2), rtol=0, atol=1e-14)
+    # a round-robin grouping (h mod H_kv) is a different function: the
+    # library pin above must reject it
+    wrong = [oracle.attention_bwd(q[:, h], k[:, h % H_kv], v[:, h % H_kv], do[:, h], 0.5,
+                                  "sliding", 5)[0] for h in range(H)]
+    tq = torch_grads_gqa(q, k, v, do, 0.5, "sliding", 5)[0]
+    assert not np.allclose(np.stack(wrong, axis=1), tq, atol=1e-6)
