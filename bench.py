@@ -25,7 +25,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        fa_fwd_fp8, timed against the 5033.2 TFLOP/s dense E4M3 peak)
        [--no-cpu-baseline] [--copy-calibration]
        python bench.py --n-sweep   (traffic-vs-N evidence, bf16 causal B=1 H=32 d=128)
-       python bench.py --bwd       (backward pass, B=1 H=32 N=16384 d=128 bf16 causal)
+       python bench.py --bwd       (backward pass, B=1 H=32 N=16384 d=128 bf16 causal;
+                                    --workload picks another bf16 shape, e.g. the
+                                    shared-head one, fa_bwd_gqa)
        python bench.py --decode    (decoding, B=8 H=32 H_kv=8 Nq=1 Nk=32768 d=128 bf16)
        python bench.py --hbm-reference   (torch sum / copy over 1 GiB, for context)
        python bench.py --record-traffic FETCH_CSV WRITE_CSV WORKLOAD "COMMAND"
@@ -343,29 +345,36 @@ def n_sweep(torch, fa):
                           "grid_threads": 32 * ((N + 255) // 256) * 512}), flush=True)
 
 
-def bwd_bench(torch, fa, si, steps: int, warmup: int):
-    """Backward pass (fa_bwd: delta, dq and dk/dv kernels) on the long-context
-    shape B=1 H=32 N=16384 d=128, bf16, causal, seeded N(0,1) q, k, v and
-    output gradient, o and lse from one fa_fwd call.  FLOPs: 2.5 x the
+def bwd_bench(torch, fa, si, steps: int, warmup: int, w=None):
+    """Backward pass (fa_bwd, or fa_bwd_gqa with shared key/value heads:
+    delta, dq and dk/dv kernels) on a bf16 workload, by default the
+    long-context shape B=1 H=32 N=16384 d=128 causal; seeded N(0,1) q, k, v
+    and output gradient, o and lse from one forward call.  FLOPs: 2.5 x the
     forward's (five N x N x d products against two), the usual count; the
     kernels issue 3.5 x (S and dP are formed in both loop kernels)."""
-    w = si.HEADLINE
-    q, k, v, do = si.make_qkv_dout(w.B, w.H, w.N, w.d, w.dtype, 1010)
+    w = w or si.HEADLINE
+    seed = 1010 if w is si.HEADLINE else w.seed + 100
+    q, k, v, do = si.make_qkv_dout_shared(w.B, w.H, w.kv_heads, w.N, w.d, w.dtype, seed)
     dev = "cuda:0"
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
     o, lse = fa.attention(qd, kd, vd, w.scale, w.mask, w.window)
-    dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+    dq = torch.empty_like(qd)
+    dk, dv = torch.empty_like(kd), torch.empty_like(vd)
     delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    call = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
-            dod.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-            w.B, w.H, w.N, w.d, float(w.scale), fa.MASKS[w.mask], int(w.window),
-            fa.FA_DTYPE_BF16, stream.cuda_stream)
+    ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            dod.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr())
+    rest = (w.N, w.d, float(w.scale), fa.MASKS[w.mask], int(w.window), fa.FA_DTYPE_BF16,
+            stream.cuda_stream)
+    if w.kv_heads == w.H:
+        entry, call = fa.fa_bwd, ptrs + (w.B, w.H) + rest
+    else:
+        entry, call = fa.fa_bwd_gqa, ptrs + (w.B, w.H, w.kv_heads) + rest
 
     def step():
-        st = fa.fa_bwd(*call)
+        st = entry(*call)
         if st != fa.FA_OK:
-            raise fa.FaError(st, "fa_bwd")
+            raise fa.FaError(st, entry.__name__)
 
     for _ in range(warmup):
         step()
@@ -387,8 +396,8 @@ def bwd_bench(torch, fa, si, steps: int, warmup: int):
         "metric": "attention bwd TFLOP/s (bf16 causal, N=16384, d=128)",
         "value": round(flops * steps / wall / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(wall * 1e3 / steps, 4),
-        "higher_is_better": True, "dtype": w.dtype, "data": "synthetic (seeded N(0,1), seed 1010)",
-        "config": {"workload": "bwd_" + w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+        "higher_is_better": True, "dtype": w.dtype, "data": "synthetic (seeded N(0,1), seed %d)" % seed,
+        "config": {"workload": "bwd_" + w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "N": w.N, "d": w.d,
                    "mask": w.mask, "flops_per_step": flops, "flop_count": "2.5 x forward"},
         "roofline": {"bound": "mfma", "achieved": round(flops / (avg * 1e-3) / 1e12, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(flops / (avg * 1e-3) / 1e12 / peak, 4),
@@ -531,7 +540,10 @@ def main():
         n_sweep(torch, fa)
         return
     if args.bwd:
-        bwd_bench(torch, fa, si, args.steps, args.warmup)
+        if w.dtype != "bf16":
+            print("bench.py --bwd times bf16 workloads", file=sys.stderr)
+            sys.exit(2)
+        bwd_bench(torch, fa, si, args.steps, args.warmup, w)
         return
     if args.decode:
         decode_bench(torch, fa, args.steps, args.warmup)

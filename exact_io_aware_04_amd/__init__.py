@@ -1,7 +1,7 @@
 """Python binding of libfa.so: the fused exact attention forward pass on
 gfx950 (MI355X).
 
-The functions named like the C ABI (``fa_fwd``, ``fa_fwd_gqa``, ``fa_fwd_fp8``, ``fa_decode``,
+The functions named like the C ABI (``fa_fwd``, ``fa_fwd_gqa``, ``fa_fwd_fp8``, ``fa_bwd_gqa``, ``fa_decode``,
 ``fa_decode_workspace_bytes``, ``fa_bwd``, ``fa_fwd_record_tiles``,
 ``fa_tile_shape``, ``fa_tile_map``, ``fa_status_string``, ``fa_last_error``,
 ``fa_probe_mfma``, ``fa_mfma_ceiling``) only marshal arguments: pointers are plain integers
@@ -60,6 +60,8 @@ def load():
     lib.fa_fwd_fp8.restype = i
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, i, i, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_gqa.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, i, i, vp]
+    lib.fa_bwd_gqa.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = ctypes.c_longlong
     lib.fa_decode.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, i, vp, ctypes.c_longlong, vp]
@@ -112,6 +114,12 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, mask_kin
            dtype, stream) -> int:
     return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, mask_kind,
                          window, dtype, stream)
+
+
+def fa_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H_kv, N, d, scale, mask_kind,
+               window, dtype, stream) -> int:
+    return load().fa_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H_kv, N, d, scale,
+                             mask_kind, window, dtype, stream)
 
 
 def fa_decode_workspace_bytes(B, H, H_kv, Nq, Nk, d) -> int:
@@ -265,14 +273,18 @@ def attention_fp8(q, k, v, scale=None, v_scale: float = 1.0, mask: str = "none",
 
 
 def attention_bwd(q, k, v, o, lse, dout, scale=None, mask: str = "none", window: int = 0):
-    """dq, dk, dv of attention for device tensors [B, H, N, d] (f16/bf16):
-    q, k, v the forward inputs, o and lse its outputs (o in the input dtype),
-    dout the gradient of the loss with respect to o.  Allocates dq, dk, dv
-    and the float32 [B, H, N] workspace with torch and calls ``fa_bwd`` on
-    the current stream."""
+    """dq, dk, dv of attention for device tensors (f16/bf16): q, o, dout
+    [B, H, N, d], k, v [B, H_kv, N, d] (H_kv dividing H; H_kv < H calls
+    ``fa_bwd_gqa``), o and lse the forward call's outputs (o in the input
+    dtype, lse float32 [B, H, N]), dout the gradient of the loss with
+    respect to o.  Allocates dq, dk, dv and the float32 [B, H, N] workspace
+    with torch and calls ``fa_bwd`` / ``fa_bwd_gqa`` on the current stream."""
     import torch
-    if not (q.dim() == 4 and q.shape == k.shape == v.shape == o.shape == dout.shape):
-        raise ValueError("q, k, v, o, dout must share one shape [B, H, N, d]")
+    if not (q.dim() == 4 and q.shape == o.shape == dout.shape and k.dim() == 4
+            and k.shape == v.shape):
+        raise ValueError("q, o, dout must be [B, H, N, d] and k, v [B, H_kv, N, d]")
+    if (k.shape[0], k.shape[2], k.shape[3]) != (q.shape[0], q.shape[2], q.shape[3]):
+        raise ValueError("k, v must match q in B, N and d")
     if lse.shape != q.shape[:3] or lse.dtype != torch.float32:
         raise ValueError("lse must be float32 [B, H, N]")
     ts = (q, k, v, o, lse, dout)
@@ -283,15 +295,23 @@ def attention_bwd(q, k, v, o, lse, dout, scale=None, mask: str = "none", window:
     if not all(t.is_contiguous() for t in ts):
         raise ValueError("all tensors must be contiguous")
     B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if H_kv < 1 or H % H_kv:
+        raise ValueError("the key/value head count %d must divide H = %d" % (H_kv, H))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dq = torch.empty_like(q)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr())
+    rest = (N, d, float(scale), MASKS[mask], int(window), _dtype_code(q.dtype), stream)
     with torch.cuda.device(q.device):
-        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                    B, H, N, d, float(scale), MASKS[mask], int(window), _dtype_code(q.dtype), stream)
+        if H_kv != H:
+            st = fa_bwd_gqa(*ptrs, B, H, H_kv, *rest)
+        else:
+            st = fa_bwd(*ptrs, B, H, *rest)
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv

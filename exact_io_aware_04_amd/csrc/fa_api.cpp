@@ -167,12 +167,14 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
 
 int check_bwd_args(const void* q, const void* k, const void* v, const void* o,
                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                   float* delta, int B, int H, int N, int d, float scale, int mask_kind,
-                   int window, int dtype) {
+                   float* delta, int B, int H, int H_kv, int N, int d, float scale,
+                   int mask_kind, int window, int dtype) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta)
     return fail(FA_ERR_INVALID_ARG, "null pointer argument");
   if (B < 1 || H < 1 || N < 1)
     return fail(FA_ERR_INVALID_ARG, "B, H and N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0)
+    return fail(FA_ERR_INVALID_ARG, "H_kv must divide H = %d (got %d)", H, H_kv);
   if (N >= (1 << 30)) return fail(FA_ERR_INVALID_ARG, "N must be < 2^30 (got %d)", N);
   if (!valid_dtype(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL && mask_kind != FA_MASK_SLIDING)
@@ -198,11 +200,12 @@ int check_bwd_args(const void* q, const void* k, const void* v, const void* o,
   if ((((uintptr_t)lse | (uintptr_t)delta) & 3u) != 0)
     return fail(FA_ERR_INVALID_ARG, "lse and delta must be 4-byte aligned");
   const size_t nm = (size_t)bh * N * d * elem_bytes(dtype);
+  const size_t nkv = (size_t)B * H_kv * N * d * elem_bytes(dtype);
   const size_t nr = (size_t)bh * N * sizeof(float);
   const void* ins[6] = {q, k, v, o, dout, lse};
-  const size_t nins[6] = {nm, nm, nm, nm, nm, nr};
+  const size_t nins[6] = {nm, nkv, nkv, nm, nm, nr};
   const void* outs[4] = {dq, dk, dv, delta};
-  const size_t nouts[4] = {nm, nm, nm, nr};
+  const size_t nouts[4] = {nm, nkv, nkv, nr};
   for (int a = 0; a < 4; ++a) {
     for (int b = 0; b < 6; ++b)
       if (overlaps(outs[a], nouts[a], ins[b], nins[b]))
@@ -347,10 +350,11 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
   return ok();
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-           const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
-           int d, float scale, int mask_kind, int window, int dtype, void* stream) {
-  int st = check_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale,
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
+               int H_kv, int N, int d, float scale, int mask_kind, int window, int dtype,
+               void* stream) {
+  int st = check_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H_kv, N, d, scale,
                           mask_kind, window, dtype);
   if (st != FA_OK) return st;
   st = check_device();
@@ -367,6 +371,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   p.dk = dk;
   p.dv = dv;
   p.BH = B * H;
+  p.kv_group = H / H_kv;
   p.N = N;
   p.mask_kind = mask_kind;
   p.window = mask_kind == FA_MASK_SLIDING ? (window < N ? window : N) : 0;
@@ -381,6 +386,13 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   hipError_t e = fa_launch_bwd(dtype, d, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+           int d, float scale, int mask_kind, int window, int dtype, void* stream) {
+  return fa_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H, N, d, scale, mask_kind,
+                    window, dtype, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

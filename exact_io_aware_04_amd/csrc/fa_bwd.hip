@@ -13,7 +13,8 @@
 //   fa_bwd_delta_kernel  D_i = <do_i, o_i> in fp32, one pass over do and o
 //   fa_bwd_dq_kernel     per 256-row query tile, over its key blocks:
 //                        S^T, dP^T, dS^T, dq^T += k^T dS^T   (lane = query)
-//   fa_bwd_dkdv_kernel   per 128-key tile, over its query blocks:
+//   fa_bwd_dkdv_kernel   per 128-key tile, over its query blocks (of every
+//                        query head that shares the key/value head):
 //                        S, dP, dS, dv^T += do^T P, dk^T += q^T dS (lane = key)
 // S and dP are formed in both loop kernels (seven matrix products per
 // query-block / key-block pair instead of five), so that no partial dq is
@@ -220,10 +221,12 @@ fa_bwd_dq_kernel(FaBwdParams p) {
   const int qb0 = q0 + wave * BR, qb1 = min(qb0 + BR, N);
   const int qi = qb0 + l32, qr = min(qi, N - 1);
 
+  // query slice bh reads key/value slice bh / g (g = H / H_kv)
   const size_t head = (size_t)bh * N * ROWB;
+  const size_t kvhead = (size_t)(bh / p.kv_group) * N * ROWB;
   const unsigned char* Qh = (const unsigned char*)p.q + head;
-  const unsigned char* Kh = (const unsigned char*)p.k + head;
-  const unsigned char* Vh = (const unsigned char*)p.v + head;
+  const unsigned char* Kh = (const unsigned char*)p.k + kvhead;
+  const unsigned char* Vh = (const unsigned char*)p.v + kvhead;
   const unsigned char* dOh = (const unsigned char*)p.dout + head;
 
   fa_u32x4 qf[NQF], dof[NQF];
@@ -332,18 +335,20 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
   const int N = p.N;
-  const int bh = blockIdx.x % p.BH, kt = blockIdx.x / p.BH;  // low key tiles see the most queries
+  // key/value slice bkv; the query slices bkv g .. bkv g + g - 1 read it
+  const int BHkv = p.BH / p.kv_group;
+  const int bkv = blockIdx.x % BHkv, kt = blockIdx.x / BHkv;  // low key tiles see the most queries
   const int k0 = kt * BW * BR, k1 = min(k0 + BW * BR, N);
   const int kw0 = k0 + wave * BR;
   const int kj = kw0 + l32, kr = min(kj, N - 1);
 
-  const size_t head = (size_t)bh * N * ROWB;
-  const unsigned char* Qh = (const unsigned char*)p.q + head;
-  const unsigned char* Kh = (const unsigned char*)p.k + head;
-  const unsigned char* Vh = (const unsigned char*)p.v + head;
-  const unsigned char* dOh = (const unsigned char*)p.dout + head;
-  const float* lse_h = p.lse + (size_t)bh * N;
-  const float* dl_h = p.delta + (size_t)bh * N;
+  const size_t kvhead = (size_t)bkv * N * ROWB;
+  const unsigned char* Kh = (const unsigned char*)p.k + kvhead;
+  const unsigned char* Vh = (const unsigned char*)p.v + kvhead;
+  const unsigned char* Qh;
+  const unsigned char* dOh;
+  const float* lse_h;
+  const float* dl_h;
 
   fa_u32x4 kf[NQF], vf[NQF];
   row_fragments<D>(Kh + (size_t)kr * ROWB, half, kf);
@@ -379,10 +384,6 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
           rsrc, (FA_AS3 void*)(wave == 0 ? &ls[b][0] : &dl[b][0]), 4, lane * 4, 0, 0, 0);
     }
   };
-  load(qlo, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
   auto step = [&](int qt, int s) {
     if (qt + 1 < qhi) load(qt + 1, s ^ 1);
     const int cls = fa_classify(qt * BB, min(qt * BB + BB, N), kw0, BR, N, p.mask_kind, p.window);
@@ -450,15 +451,28 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
     barrier_nofence();
   };
-  for (int qt = qlo;;) {
-    step(qt, 0);
-    if (++qt >= qhi) break;
-    step(qt, 1);
-    if (++qt >= qhi) break;
+  // every query slice of the group in turn, all into the same dk, dv (the
+  // last step of a slice ends with a barrier, so its slots are free)
+  for (int j = 0; j < p.kv_group; ++j) {
+    const int bh = bkv * p.kv_group + j;
+    const size_t head = (size_t)bh * N * ROWB;
+    Qh = (const unsigned char*)p.q + head;
+    dOh = (const unsigned char*)p.dout + head;
+    lse_h = p.lse + (size_t)bh * N;
+    dl_h = p.delta + (size_t)bh * N;
+    load(qlo, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int qt = qlo;;) {
+      step(qt, 0);
+      if (++qt >= qhi) break;
+      step(qt, 1);
+      if (++qt >= qhi) break;
+    }
   }
   if (kj < N) {
-    store_rows<DT, D>(p.dk, (size_t)bh * N + kj, dka, p.scale, half);
-    store_rows<DT, D>(p.dv, (size_t)bh * N + kj, dva, 1.f, half);
+    store_rows<DT, D>(p.dk, (size_t)bkv * N + kj, dka, p.scale, half);
+    store_rows<DT, D>(p.dv, (size_t)bkv * N + kj, dva, 1.f, half);
   }
 }
 
@@ -469,7 +483,8 @@ hipError_t launch_bwd(const FaBwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((fa_bwd_delta_kernel<DT, D>), dim3(dgrid), dim3(256), 0, stream, p);
   hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D>), dim3((unsigned)(p.BH * p.n_q_tiles)), dim3(BWQ * 64),
                      0, stream, p);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D>), dim3((unsigned)(p.BH * p.n_k_tiles)), dim3(BW * 64),
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D>), dim3((unsigned)(p.BH / p.kv_group * p.n_k_tiles)),
+                     dim3(BW * 64),
                      0, stream, p);
   return hipGetLastError();
 }

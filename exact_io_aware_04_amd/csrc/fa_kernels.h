@@ -37,7 +37,9 @@ struct FaBwdParams {
   void* dq;
   void* dk;
   void* dv;
-  int BH;
+  int BH;                 // batch * query heads
+  int kv_group;           // query heads per key/value head (H / H_kv): query
+                          // slice bh reads key/value slice bh / kv_group
   int N;
   int mask_kind;
   int window;

@@ -205,6 +205,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int mask_kind, int window, int dtype, void* stream);
 
 /*
+ * Backward pass of fa_fwd_gqa: the same gradients when query head h of batch
+ * entry b reads key/value head h / (H / H_kv).  dq is per query head as in
+ * fa_bwd; dk and dv of a key/value head sum, over the H / H_kv query heads
+ * that read it, the terms fa_bwd would give each of them (the chain rule
+ * through the shared operand):
+ *
+ *   dk[b,g,j] = scale sum_{h: h/(H/H_kv) = g} sum_i dS^h_ij q[b,h,i]
+ *   dv[b,g,j] = sum_{h: h/(H/H_kv) = g} sum_i P^h_ij dout[b,h,i]
+ *
+ *   k, v, dk, dv  [B][H_kv][N][d] of dtype; every other argument as in fa_bwd
+ *   H_kv          1 <= H_kv <= H, dividing H (else FA_ERR_INVALID_ARG)
+ * A key/value head's dk, dv accumulate in fp32 over all of its query heads
+ * and are rounded once.  fa_bwd is this call with H_kv = H.
+ */
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+               float* delta, int B, int H, int H_kv, int N, int d, float scale,
+               int mask_kind, int window, int dtype, void* stream);
+
+/*
  * Same as fa_fwd, and records the tile decisions the kernel took: for every
  * (b, h), row block rb of tile_rows rows and key block kb of tile_keys keys
  * (see fa_tile_shape), tiles[((b*H + h) * R + rb) * C + kb] is set to

@@ -116,6 +116,17 @@ def make_qkv_shared(B: int, H: int, H_kv: int, N: int, d: int, dtype: str, seed:
     return tuple(out)
 
 
+def make_qkv_dout_shared(B: int, H: int, H_kv: int, N: int, d: int, dtype: str, seed: int):
+    """q [B, H, N, d], k, v [B, H_kv, N, d] and an output gradient dout
+    [B, H, N, d]: the same recipe, drawn in that order."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for heads in (H, H_kv, H_kv, H):
+        x = rng.standard_normal((B, heads, N, d), dtype=np.float32)
+        out.append(torch.from_numpy(x).to(DTYPES[dtype]).contiguous())
+    return tuple(out)
+
+
 def _as_codes(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
 

@@ -329,3 +329,33 @@ def test_fp8_torch_wrapper_rejects_bad_tensors():
         fa.attention_fp8(q, q, q)          # host tensors
     with pytest.raises(ValueError):
         fa.attention_fp8(q.float(), q, q)  # not E4M3
+
+
+# ---- backward pass with shared key/value heads (fa_bwd_gqa) ---------------------
+def call_bwd_gqa(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=LS, dout=DO_, dq=DQ, dk=DK, dv=DV, delta=DL, B=1, H=8,
+                H_kv=2, N=100, d=128, scale=0.1, mask_kind=fa.FA_MASK_CAUSAL, window=0,
+                dtype=fa.FA_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_bwd_gqa(*(args[n] for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv",
+                                             "delta", "B", "H", "H_kv", "N", "d", "scale",
+                                             "mask_kind", "window", "dtype", "stream")))
+
+
+@pytest.mark.parametrize("kw", [dict(H_kv=0), dict(H_kv=3), dict(H_kv=16), dict(H_kv=-1),
+                                dict(k=0), dict(dk=0), dict(N=0)], ids=str)
+def test_bwd_gqa_invalid_arguments_are_rejected_on_the_host(kw):
+    assert call_bwd_gqa(**kw) == fa.FA_ERR_INVALID_ARG, fa.fa_last_error()
+
+
+def test_bwd_gqa_overlap_checks_use_the_key_value_head_count():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    # dk holds B*H_kv*N*d bf16 = 2 * 100 * 128 * 2 bytes: dv right after it is
+    # fine, dv starting inside it overlaps
+    kvbytes = 2 * 100 * 128 * 2
+    assert call_bwd_gqa(dv=DK + kvbytes) in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP), fa.fa_last_error()
+    assert call_bwd_gqa(dv=DK + kvbytes - 16) == fa.FA_ERR_INVALID_ARG
+    assert call_bwd_gqa(H_kv=8) in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
+    assert call_bwd_gqa(H_kv=1) in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)

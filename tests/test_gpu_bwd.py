@@ -140,3 +140,74 @@ def test_bwd_errors_before_launch():
     with pytest.raises(fa.FaError) as e:
         fa.attention_bwd(z, z, z, z, lse, z, mask="sliding", window=0)
     assert e.value.status == fa.FA_ERR_INVALID_ARG
+
+
+# ---- shared key/value heads (fa_bwd_gqa) --------------------------------------
+HEADS = [(4, 1), (4, 2), (6, 3)]  # (H, H_kv)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 100)])
+def test_bwd_shared_heads_against_oracle(dtype, d, mask, window):
+    for (H, H_kv), N in zip(HEADS, [1, 257, 1000]):
+        say("bwd shared heads", dtype, d, mask, window, H, H_kv, N)
+        q, k, v, do = si.make_qkv_dout_shared(2, H, H_kv, N, d, dtype, 9700 + N + d + H_kv)
+        scale = 1.0 / math.sqrt(d)
+        dq, dk, dv = grads(q, k, v, do, scale, mask, window)
+        assert dk.shape == k.shape and dv.shape == v.shape
+        rq, rk, rv = oracle.attention_bwd_gqa(q, k, v, do, scale, mask, window)
+        for nm, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            check(g, r, dtype, "%s H=%d H_kv=%d N=%d" % (nm, H, H_kv, N))
+
+
+@pytest.mark.parametrize("H,H_kv", [(8, 1), (8, 2)])
+def test_bwd_shared_heads_match_copied_heads(H, H_kv):
+    """dq equals the plain backward pass on key/value heads copied out to
+    every query head bit for bit (same kernel arithmetic); dk, dv equal the
+    copies' gradients summed over each group up to rounding (the shared pass
+    sums in fp32 and rounds once, the copies round per head)."""
+    N, d = 600, 128
+    q, k, v, do = si.make_qkv_dout_shared(1, H, H_kv, N, d, "bf16", 9800 + H_kv)
+    g = H // H_kv
+    kc, vc = (t.repeat_interleave(g, dim=1).contiguous() for t in (k, v))
+    for mask, window in (("causal", 0), ("sliding", 50)):
+        say("bwd copied heads", H, H_kv, mask)
+        dq, dk, dv = grads(q, k, v, do, 0.1, mask, window)
+        cq, ck, cv = grads(q, kc, vc, do, 0.1, mask, window)
+        assert torch.equal(dq, cq), mask
+        sk = ck.float().reshape(1, H_kv, g, N, d).sum(dim=2).double().cpu().numpy()
+        sv = cv.float().reshape(1, H_kv, g, N, d).sum(dim=2).double().cpu().numpy()
+        check(dk, sk, "bf16", "dk vs copies %s" % mask)
+        check(dv, sv, "bf16", "dv vs copies %s" % mask)
+
+
+def test_bwd_shared_heads_full_size_sampled():
+    """B=1 H=32 H_kv=8 N=16384 d=128 bf16 causal: sampled query rows (dq) of
+    two query heads and sampled keys (dk, dv summed over the four query
+    heads) of the first key/value head against the oracle."""
+    B, H, H_kv, N, d = 1, 32, 8, 16384, 128
+    g = H // H_kv
+    say("bwd shared heads full size")
+    q, k, v, do = si.make_qkv_dout_shared(B, H, H_kv, N, d, "bf16", 9900)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = grads(q, k, v, do, scale, "causal", 0)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+    rng = np.random.default_rng(9901)
+    sel = np.array(sorted(set([0, 1, 127, 128, 8191, N - 1] + rng.integers(0, N, size=20).tolist())),
+                   dtype=np.int64)
+    idx = torch.from_numpy(sel).to(DEV)
+    for h in (0, g - 1):
+        say("bwd shared heads full size dq head", h)
+        rq = oracle.attention_bwd_rows(q[0, h], k[0, 0], v[0, 0], do[0, h], sel, scale, "causal")
+        check(dq[0, h].index_select(0, idx), rq, "bf16", "dq h%d" % h)
+    rk = np.zeros((len(sel), d))
+    rv = np.zeros((len(sel), d))
+    for h in range(g):
+        say("bwd shared heads full size keys, query head", h)
+        a, b = oracle.attention_bwd_keys(q[0, h], k[0, 0], v[0, 0], do[0, h], sel, scale, "causal")
+        rk += a
+        rv += b
+    check(dk[0, 0].index_select(0, idx), rk, "bf16", "dk kv0")
+    check(dv[0, 0].index_select(0, idx), rv, "bf16", "dv kv0")
