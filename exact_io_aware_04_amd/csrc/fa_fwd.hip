@@ -40,7 +40,8 @@
 //    8-byte pieces addressed by lanes 4t + j/4, t = 0..3), at the keys that
 //    match the accumulator's row order, so no data moves between the two
 //    matrix products.  The row sums of the rounded probabilities come from
-//    the matrix core too (an all-ones operand times the same P^T operands).
+//    the matrix core too: one 16x16x32 product per P^T operand, with an A
+//    operand of ones and zeros that picks each lane's own row.
 //  * The softmax runs in base 2.  The reference maximum is set to the exact
 //    row maximum on a row's first block and on boundary blocks, and otherwise
 //    kept while every probability stays below 2^8 (checked through the lane
@@ -140,6 +141,34 @@ __device__ __forceinline__ void store_output(const FaFwdParams& p, const fa_f32x
 // ---------------------------------------------------------------------------
 
 
+// Row sums of the rounded probabilities on the matrix core.  A P^T operand
+// of the 32x32x16 product (lane l: row l mod 32, 8 keys of half l / 32) is
+// also a valid B operand of v_mfma_f32_16x16x32_{bf16,f16}, where lane l
+// holds 8 of the 32 contraction indices of slice l / 16 for output column
+// l mod 16; the A operand of lane l covers row l mod 16 over the same slice.
+// Slices 0 and 2 hold rows 0..15 of P, slices 1 and 3 rows 16..31.  An A
+// operand that is all ones in the lanes where slice parity ((l >> 4) & 1)
+// equals ((l >> 2) & 1), zero elsewhere, makes output rows 0-3 and 8-11 the
+// sums of rows n and rows 4-7 and 12-15 those of rows n + 16, and lane l
+// holds rows 4(l / 16)..+3 of column l mod 16: every register of the 4-word
+// accumulator then carries the sum of the lane's own row l mod 32.  Half the
+// matrix-core cycles of a 32x32x16 product.
+template <int DT>
+__device__ __forceinline__ fa_u32x4 rowsum_selector(int lane) {
+  constexpr unsigned ONE2 = DT == 2 ? 0x3F803F80u : 0x3C003C00u;
+  const unsigned v = (((lane >> 4) ^ (lane >> 2)) & 1) ? 0u : ONE2;
+  return fa_u32x4{v, v, v, v};
+}
+template <int DT>
+__device__ __forceinline__ fa_f32x4 rowsum_mma(fa_u32x4 sel, fa_u32x4 b, fa_f32x4 c) {
+  if constexpr (DT == 2)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        __builtin_bit_cast(fa_bf16x8, sel), __builtin_bit_cast(fa_bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        __builtin_bit_cast(fa_f16x8, sel), __builtin_bit_cast(fa_f16x8, b), c, 0, 0, 0);
+}
+
 // Matrix phase of one wavefront: S^T = K Q^T over the current key block (QK)
 // and O^T += V^T P^T over the previous one (PV), as one software-pipelined
 // sequence of products whose LDS operands are read FA_OPND_AHEAD products
@@ -149,8 +178,8 @@ __device__ __forceinline__ void store_output(const FaFwdParams& p, const fa_f32x
 // still executing.  Product order: Q K by contraction slice s, then key
 // group kb (the score accumulators starting from sc0); then P V by (kb,
 // half t), then output block cb, so consecutive products update different
-// accumulators; last, four products of an all-ones operand with the P^T
-// operands add the block's rounded probabilities to the row sums lsum.  The
+// accumulators; last, four row-sum products (rowsum_mma) add the block's
+// rounded probabilities to the row sums lsum.  The
 // K operand of (s, kb) is one 16-byte read of row
 // 32kb + l32, chunk 2s + half; the V^T operand of (kb, t, cb) two
 // transposing reads at rows 32kb + 16t + 4half + 0..3 and + 8 (the keys of
@@ -158,7 +187,8 @@ __device__ __forceinline__ void store_output(const FaFwdParams& p, const fa_f32x
 #define FA_OPND_AHEAD 6
 template <int DT, int D>
 __device__ __forceinline__ void matrix_phase(fa_f32x16 (&acc)[D / 32], fa_f32x16 (&sc)[2],
-                                             fa_f32x16& lsum, const fa_f32x16& sc0,
+                                             fa_f32x4& lsum, const fa_u32x4& sel,
+                                             const fa_f32x16& sc0,
                                              const fa_u32x4 (&pf)[2][2], const fa_u32x4 (&qf)[D / 16],
                                              const FA_AS3 unsigned char* kcur,
                                              const FA_AS3 unsigned char* vcur,
@@ -199,14 +229,11 @@ __device__ __forceinline__ void matrix_phase(fa_f32x16 (&acc)[D / 32], fa_f32x16
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  // row sums of the rounded probabilities: an all-ones A operand times the
-  // same P^T operands (every lane then holds its row's sum in every register)
-  constexpr unsigned ONE2 = DT == 2 ? 0x3F803F80u : 0x3C003C00u;
-  const fa_u32x4 ones = {ONE2, ONE2, ONE2, ONE2};
+  // row sums of the rounded probabilities
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) lsum = mma16<DT>(ones, pf[kb][t], lsum);
+    for (int t = 0; t < 2; ++t) lsum = rowsum_mma<DT>(sel, pf[kb][t], lsum);
 }
 
 // Eight wavefronts, 32 query rows each, two per SIMD.  The two wavefronts of
@@ -323,9 +350,8 @@ fa_fwd16_kernel(FaFwdParams p) {
   // reference (base 2) and this lane's sum of unrounded probabilities; the
   // row sums of the rounded ones accumulate on the matrix core, in lsum
   float m_ref = FA_NEG_INF, l_lane = 0.f;
-  fa_f32x16 lsum;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) lsum[r] = 0.f;
+  fa_f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
+  const fa_u32x4 sel = rowsum_selector<DT>(lane);
   const float c2 = p.scale_log2;
   const int n_row_blocks = (N + FA_ROW_BLOCK - 1) / FA_ROW_BLOCK;
   const int n_key_blocks = (N + BC - 1) / BC;
@@ -360,7 +386,7 @@ fa_fwd16_kernel(FaFwdParams p) {
   // place): the probabilities of a skipped block are 0, which adds exactly
   // 0 to O, and the scores of a skipped block are never used.
   auto phase_mfma = [&](int ks, int vs) {
-    matrix_phase<DT, D>(acc, sc, lsum, sc0, pf, qf, kbuf(ks), vbuf(vs), kread, vread);
+    matrix_phase<DT, D>(acc, sc, lsum, sel, sc0, pf, qf, kbuf(ks), vbuf(vs), kread, vread);
   };
   // Softmax phase of block kt (classification cls).  Fast path (fully
   // visible block, row already started): p = 2^t straight from the scores;
@@ -404,7 +430,7 @@ fa_fwd16_kernel(FaFwdParams p) {
       m_ref = m_new;
       l_lane *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) lsum[r] *= alpha;
+      for (int r = 0; r < 4; ++r) lsum[r] *= alpha;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -631,9 +657,8 @@ fa_fwd16_wide_kernel(FaFwdParams p) {
     asm volatile("" : "+a"(acc[cb]));  // placement only: the matrix core's AGPRs
   }
   float m_ref = FA_NEG_INF, l_lane = 0.f;
-  fa_f32x16 lsum;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) lsum[r] = 0.f;
+  fa_f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
+  const fa_u32x4 sel = rowsum_selector<DT>(lane);
   const float c2 = p.scale_log2;
   const float inv_c2 = 1.f / p.scale_log2;
   const int n_row_blocks = (N + FA_ROW_BLOCK - 1) / FA_ROW_BLOCK;
@@ -647,8 +672,6 @@ fa_fwd16_wide_kernel(FaFwdParams p) {
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int t = 0; t < 2; ++t) pf[kb][t] = fa_u32x4{0u, 0u, 0u, 0u};
-  constexpr unsigned ONE2 = DT == 2 ? 0x3F803F80u : 0x3C003C00u;
-  const fa_u32x4 ones = {ONE2, ONE2, ONE2, ONE2};
 
   // One step (K slot s holds K(kt), V slot s holds V(kt-1)).
   auto step = [&](int kt, int s) {
@@ -713,7 +736,7 @@ fa_fwd16_wide_kernel(FaFwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) lsum = mma16<DT>(ones, pf[kb][t], lsum);
+        for (int t = 0; t < 2; ++t) lsum = rowsum_mma<DT>(sel, pf[kb][t], lsum);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -756,7 +779,7 @@ fa_fwd16_wide_kernel(FaFwdParams p) {
           const float alpha = m_new > m_ref ? (m_ref == FA_NEG_INF ? 0.f : exp2_hw(m_ref - m_new)) : 1.f;
           l_lane *= alpha;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) lsum[r] *= alpha;
+          for (int r = 0; r < 4; ++r) lsum[r] *= alpha;
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
