@@ -31,6 +31,8 @@
 // both without bank conflicts (see bswz).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "tile_class.h"
@@ -42,6 +44,7 @@ constexpr int BWQ = FA_BWD_DQ_WAVES;  // wavefronts per workgroup, dq pass
 constexpr int BR = 32;            // rows (or keys) per wavefront
 constexpr int BB = 64;            // rows (or keys) per streamed block
 constexpr float LOG2E = 1.44269504088896340736f;
+#define FA_BWD_GRAD_AHEAD 6       // dk/dv gradient products: operand reads ahead
 
 // Chunk swizzle of a streamed block row r (chunk position = chunk ^ bswz(r)).
 // 16-byte row reads take one chunk of 16 consecutive rows per 16 lanes;
@@ -258,7 +261,10 @@ fa_bwd_dq_kernel(FaBwdParams p) {
       load_block<D, BWQ>(Vh, (kt + 1) * BB, N, loff, vbuf(s ^ 1), wave);
     }
     const int cls = fa_classify(qb0, qb1, kt * BB, BB, N, p.mask_kind, p.window);
-    if (cls != FA_TILE_SKIP) {
+    // one body per block class, so the (wave-uniform) class is tested once per
+    // block rather than once per score
+    auto compute = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
       const FA_AS3 unsigned char* kc = kbuf(s);
       const FA_AS3 unsigned char* vc = vbuf(s);
       // S^T = K Q^T and dP^T - D = V dO^T - D (keys x rows)
@@ -289,7 +295,7 @@ fa_bwd_dq_kernel(FaBwdParams p) {
         for (int r = 0; r < 16; ++r) {
           const int j = kt * BB + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
           float pr = exp2_hw(__builtin_fmaf(sc[kb][r], c2, -lse2));
-          if (cls == FA_TILE_PARTIAL && !visible(qi, j, N, p.mask_kind, p.window)) pr = 0.f;
+          if (MASKED && !visible(qi, j, N, p.mask_kind, p.window)) pr = 0.f;
           ds[r] = pr * dp[kb][r];
         }
         dsf[kb][0] = pack8<DT>(&ds[0]);
@@ -305,7 +311,11 @@ fa_bwd_dq_kernel(FaBwdParams p) {
             const FA_AS3 unsigned char* blk = kc + (32 * kb + 16 * t) * ROWB;
             acc[cb] = mma16<DT>(tr_operand(blk, rd.trlo[cb], rd.trhi[cb]), dsf[kb][t], acc[cb]);
           }
-    }
+    };
+    if (cls == FA_TILE_PARTIAL)
+      compute(std::true_type{});
+    else if (cls == FA_TILE_FULL)
+      compute(std::false_type{});
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
     barrier_nofence();
   };
@@ -387,7 +397,9 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
   auto step = [&](int qt, int s) {
     if (qt + 1 < qhi) load(qt + 1, s ^ 1);
     const int cls = fa_classify(qt * BB, min(qt * BB + BB, N), kw0, BR, N, p.mask_kind, p.window);
-    if (cls != FA_TILE_SKIP) {
+    // one body per block class (see the dq kernel)
+    auto compute = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
       const FA_AS3 unsigned char* qc = qbuf(s);
       const FA_AS3 unsigned char* oc = obuf(s);
       // S = Q K^T and dP - D = dO V^T - D (rows x keys); s[qb][r] is row
@@ -426,7 +438,7 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
             const int r = 4 * a + e;
             const int i = qt * BB + 32 * qb + 8 * a + 4 * half + e;
             float pv = exp2_hw(__builtin_fmaf(sc[qb][r], c2, -l4[e] * LOG2E));
-            if (cls == FA_TILE_PARTIAL && !visible(i, kj, N, p.mask_kind, p.window)) pv = 0.f;
+            if (MASKED && !visible(i, kj, N, p.mask_kind, p.window)) pv = 0.f;
             pr[r] = pv;
             ds[r] = pv * dp[qb][r];
           }
@@ -436,18 +448,39 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
         dsf[qb][0] = pack8<DT>(&ds[0]);
         dsf[qb][1] = pack8<DT>(&ds[8]);
       }
-      // dv^T += dO^T P, dk^T += Q^T dS
+      // dv^T += dO^T P, dk^T += Q^T dS.  Product j: (qb, t, cb) = j / 2, dv
+      // (j even) or dk (j odd); its transposed operand is read R products
+      // ahead, so the wave (alone on its SIMD) does not wait out the LDS
+      // latency before every product.  The group barriers keep that order.
+      {
+        constexpr int R = FA_BWD_GRAD_AHEAD, NG = 2 * NQB * 2 * NCB;
+        fa_u32x4 op[R + 1];
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
+        for (int i = 0; i < NG + R; ++i) {
+          if (i < NG) {
+            const int g = i / 2, cb = g % NCB, t = (g / NCB) % 2, qb = g / NCB / 2;
             const int rb = (32 * qb + 16 * t) * ROWB;
-            dva[cb] = mma16<DT>(tr_operand(oc + rb, rd.trlo[cb], rd.trhi[cb]), pf[qb][t], dva[cb]);
-            dka[cb] = mma16<DT>(tr_operand(qc + rb, rd.trlo[cb], rd.trhi[cb]), dsf[qb][t], dka[cb]);
+            op[i % (R + 1)] = tr_operand((i & 1 ? qc : oc) + rb, rd.trlo[cb], rd.trhi[cb]);
           }
-    }
+          if (i >= R) {
+            const int j = i - R, g = j / 2, cb = g % NCB, t = (g / NCB) % 2, qb = g / NCB / 2;
+            if (j & 1)
+              dka[cb] = mma16<DT>(op[j % (R + 1)], dsf[qb][t], dka[cb]);
+            else
+              dva[cb] = mma16<DT>(op[j % (R + 1)], pf[qb][t], dva[cb]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NG + R; ++i) {
+          if (i < NG) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          if (i >= R) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      }
+    };
+    if (cls == FA_TILE_PARTIAL)
+      compute(std::true_type{});
+    else if (cls == FA_TILE_FULL)
+      compute(std::false_type{});
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
     barrier_nofence();
   };
