@@ -106,6 +106,15 @@ int check_args(const void* q, const void* k, const void* v, void* o, float* lse,
 // Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];
+std::atomic<int> g_cus[kMaxDevices];  // compute units per device (0: not yet read)
+
+// compute units of the current device (check_device has run)
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  const int n = g_cus[dev].load(std::memory_order_relaxed);
+  return n > 0 ? n : 256;
+}
 
 int check_device() {
   int dev = -1;
@@ -120,6 +129,7 @@ int check_device() {
     if (e != hipSuccess)
       return fail(FA_ERR_NO_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
     state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
     g_arch_ok[dev].store(state, std::memory_order_relaxed);
   }
   if (state != 1) return fail(FA_ERR_NO_DEVICE, "device %d is not gfx950", dev);
@@ -383,6 +393,22 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const
   p.n_q_tiles = (N + FA_BWD_DQ_WAVES * 32 - 1) / (FA_BWD_DQ_WAVES * 32);
   p.n_k_tiles = (N + FA_BWD_WAVES * 32 - 1) / (FA_BWD_WAVES * 32);
   p.heavy_first = mask_kind != FA_MASK_NONE ? 1 : 0;
+  // Few key/value heads leave the dk/dv pass with few workgroups (one per
+  // key/value head and 128-key tile), each running all g = H / H_kv query
+  // heads.  Then the query heads are split over kv_parts workgroups per tile
+  // (aiming at four workgroups per compute unit), whose fp32 partial sums
+  // go to dq's memory -- free until the dq pass, which runs last -- and are
+  // added by a small kernel.  The partials take 8 kv_parts B H_kv N d bytes
+  // of dq's 2 B H N d, hence kv_parts <= g / 4.
+  {
+    const long long wgs = (long long)B * H_kv * p.n_k_tiles;
+    const long long want = 4LL * device_cus();
+    const int cap = p.kv_group / 4;
+    int parts = 1;
+    if (cap >= 2 && wgs < want) parts = (int)std::min<long long>(cap, (want + wgs - 1) / wgs);
+    p.kv_parts = parts;
+    p.part_scratch = parts > 1 ? (float*)dq : nullptr;
+  }
   hipError_t e = fa_launch_bwd(dtype, d, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();

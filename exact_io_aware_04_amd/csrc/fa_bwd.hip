@@ -170,6 +170,19 @@ __device__ __forceinline__ void store_rows(void* out, size_t row, const fa_f32x1
     }
 }
 
+// The same accumulators as fp32 (row = 32-bit elements of one [D] row).
+template <int D>
+__device__ __forceinline__ void store_rows_f32(float* dst, const fa_f32x16 (&acc)[D / 32], int half) {
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = cb * 32 + 8 * g + 4 * half;
+      *(fa_f32x4*)(dst + c) = fa_f32x4{acc[cb][4 * g], acc[cb][4 * g + 1], acc[cb][4 * g + 2],
+                                       acc[cb][4 * g + 3]};
+    }
+}
+
 // ---------------------------------------------------------------------------
 // D_i = <do_i, o_i>
 // ---------------------------------------------------------------------------
@@ -345,9 +358,13 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
   const int N = p.N;
-  // key/value slice bkv; the query slices bkv g .. bkv g + g - 1 read it
+  // key/value slice bkv; the query slices bkv g .. bkv g + g - 1 read it, and
+  // this workgroup takes those of part `part` (low key tiles, which see the
+  // most queries, come first)
   const int BHkv = p.BH / p.kv_group;
-  const int bkv = blockIdx.x % BHkv, kt = blockIdx.x / BHkv;  // low key tiles see the most queries
+  const int bkv = blockIdx.x % BHkv, rest = blockIdx.x / BHkv;
+  const int part = rest % p.kv_parts, kt = rest / p.kv_parts;
+  const int j_lo = part * p.kv_group / p.kv_parts, j_hi = (part + 1) * p.kv_group / p.kv_parts;
   const int k0 = kt * BW * BR, k1 = min(k0 + BW * BR, N);
   const int kw0 = k0 + wave * BR;
   const int kj = kw0 + l32, kr = min(kj, N - 1);
@@ -484,9 +501,9 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
     barrier_nofence();
   };
-  // every query slice of the group in turn, all into the same dk, dv (the
+  // every query slice of the part in turn, all into the same dk, dv (the
   // last step of a slice ends with a barrier, so its slots are free)
-  for (int j = 0; j < p.kv_group; ++j) {
+  for (int j = j_lo; j < j_hi; ++j) {
     const int bh = bkv * p.kv_group + j;
     const size_t head = (size_t)bh * N * ROWB;
     Qh = (const unsigned char*)p.q + head;
@@ -503,10 +520,43 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
       if (++qt >= qhi) break;
     }
   }
-  if (kj < N) {
+  if (kj >= N) return;
+  if (p.kv_parts == 1) {
     store_rows<DT, D>(p.dk, (size_t)bkv * N + kj, dka, p.scale, half);
     store_rows<DT, D>(p.dv, (size_t)bkv * N + kj, dva, 1.f, half);
+  } else {
+    const size_t plane = (size_t)p.kv_parts * BHkv * N * D;  // floats per tensor
+    const size_t row = ((size_t)part * BHkv + bkv) * N + kj;
+    store_rows_f32<D>(p.part_scratch + row * D, dka, half);
+    store_rows_f32<D>(p.part_scratch + plane + row * D, dva, half);
   }
+}
+
+// dk, dv = the sums of the kv_parts fp32 partials (dk times scale), rounded
+// once to the input type; thread t takes 8 consecutive elements of dk (first
+// half of the grid) or dv (second half)
+template <int DT>
+__global__ void __launch_bounds__(256) fa_bwd_combine_kernel(FaBwdParams p, long long n8) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= 2 * n8) return;
+  const bool is_dv = t >= n8;
+  const long long e = (is_dv ? t - n8 : t) * 8;     // element index in [BHkv][N][d]
+  const size_t plane = (size_t)p.kv_parts * n8 * 8;  // floats per tensor
+  const float* src = p.part_scratch + (is_dv ? plane : 0) + e;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < p.kv_parts; ++j) {
+    const fa_f32x4 a = *(const fa_f32x4*)(src + (size_t)j * n8 * 8);
+    const fa_f32x4 b = *(const fa_f32x4*)(src + (size_t)j * n8 * 8 + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] += a[i];
+      acc[4 + i] += b[i];
+    }
+  }
+  const float mul = is_dv ? 1.f : p.scale;
+  unsigned char* dst = (unsigned char*)(is_dv ? p.dv : p.dk) + e * 2;
+  *(fa_u32x2*)dst = pack4<DT>(acc[0] * mul, acc[1] * mul, acc[2] * mul, acc[3] * mul);
+  *(fa_u32x2*)(dst + 8) = pack4<DT>(acc[4] * mul, acc[5] * mul, acc[6] * mul, acc[7] * mul);
 }
 
 template <int DT, int D>
@@ -514,10 +564,17 @@ hipError_t launch_bwd(const FaBwdParams& p, hipStream_t stream) {
   const long long rows = (long long)p.BH * p.N;
   const unsigned dgrid = (unsigned)((rows + 256 / (D / 8) - 1) / (256 / (D / 8)));
   hipLaunchKernelGGL((fa_bwd_delta_kernel<DT, D>), dim3(dgrid), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D>), dim3((unsigned)(p.BH * p.n_q_tiles)), dim3(BWQ * 64),
+  // dk/dv (and the sum of its partials) before dq: with kv_parts > 1 the
+  // partials live in dq's memory, which the dq pass then overwrites
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D>),
+                     dim3((unsigned)(p.BH / p.kv_group * p.n_k_tiles * p.kv_parts)), dim3(BW * 64),
                      0, stream, p);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D>), dim3((unsigned)(p.BH / p.kv_group * p.n_k_tiles)),
-                     dim3(BW * 64),
+  if (p.kv_parts > 1) {
+    const long long n8 = (long long)(p.BH / p.kv_group) * p.N * D / 8;
+    hipLaunchKernelGGL((fa_bwd_combine_kernel<DT>), dim3((unsigned)((2 * n8 + 255) / 256)), dim3(256),
+                       0, stream, p, n8);
+  }
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D>), dim3((unsigned)(p.BH * p.n_q_tiles)), dim3(BWQ * 64),
                      0, stream, p);
   return hipGetLastError();
 }

@@ -48,6 +48,11 @@ struct FaBwdParams {
   int n_q_tiles;          // ceil(N / (FA_BWD_DQ_WAVES * 32)): query tiles of the dq pass
   int n_k_tiles;          // ceil(N / (FA_BWD_WAVES * 32)): key tiles of the dk/dv pass
   int heavy_first;        // 1: longest query tiles of the dq pass first (masks)
+  int kv_parts;           // dk/dv workgroups per key tile: part j of kv_parts takes
+                          // query heads [j g / kv_parts, (j + 1) g / kv_parts) of
+                          // the g = kv_group heads that share the key/value head
+  float* part_scratch;    // kv_parts > 1: fp32 partial sums of dk (not yet times
+                          // scale) and then of dv, each [kv_parts][BH / kv_group][N][d]
 };
 constexpr int FA_BWD_WAVES = 4;     // wavefronts per workgroup, dk/dv pass (one per SIMD)
 constexpr int FA_BWD_DQ_WAVES = 8;  // wavefronts per workgroup, dq pass (two per SIMD)

@@ -217,7 +217,13 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  *   k, v, dk, dv  [B][H_kv][N][d] of dtype; every other argument as in fa_bwd
  *   H_kv          1 <= H_kv <= H, dividing H (else FA_ERR_INVALID_ARG)
  * A key/value head's dk, dv accumulate in fp32 over all of its query heads
- * and are rounded once.  fa_bwd is this call with H_kv = H.
+ * and are rounded once.  With 8 or more query heads per key/value head and
+ * fewer than four dk/dv workgroups (one per key/value head and 128 keys) per
+ * compute unit, the query heads of a key tile are split over up to
+ * (H / H_kv) / 4 workgroups whose fp32 partial sums are kept in dq's memory
+ * until a final kernel adds them (dq is written afterwards): the sum order,
+ * and so the last bit of dk and dv, depends on that split.  fa_bwd is this
+ * call with H_kv = H.
  */
 int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                const float* lse, const void* dout, void* dq, void* dk, void* dv,

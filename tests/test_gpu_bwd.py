@@ -182,6 +182,47 @@ def test_bwd_shared_heads_match_copied_heads(H, H_kv):
         check(dv, sv, "bf16", "dv vs copies %s" % mask)
 
 
+# Groups of 8 or more query heads per key/value head with few key tiles: the
+# dk/dv pass splits each tile's query heads over kv_parts workgroups (at most
+# g / 4) and sums their fp32 partials.  (H, H_kv, N): parts 8 (g = 32, N =
+# 1000), 2 uneven (g = 9: heads 0-3 and 4-8), 2 (g = 8 with two key/value
+# heads), 3 (g = 12).
+SPLIT_HEADS = [(32, 1, 1000), (9, 1, 333), (16, 2, 700), (12, 1, 129)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 100)])
+def test_bwd_split_query_heads_against_oracle(dtype, d, mask, window):
+    for H, H_kv, N in SPLIT_HEADS:
+        say("bwd split query heads", dtype, d, mask, window, H, H_kv, N)
+        q, k, v, do = si.make_qkv_dout_shared(1, H, H_kv, N, d, dtype, 9750 + N + d + H)
+        scale = 1.0 / math.sqrt(d)
+        dq, dk, dv = grads(q, k, v, do, scale, mask, window)
+        rq, rk, rv = oracle.attention_bwd_gqa(q, k, v, do, scale, mask, window)
+        for nm, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            check(g, r, dtype, "%s H=%d H_kv=%d N=%d" % (nm, H, H_kv, N))
+
+
+def test_bwd_multi_query_full_size_matches_copied_heads():
+    """B=1 H=32 H_kv=1 N=16384 d=128 bf16 causal, the benchmarked multi-query
+    shape (dk/dv split over 8 workgroups per key tile): dq equals the plain
+    pass on the key/value head copied to all 32 query heads bit for bit; dk,
+    dv equal the copies' gradients summed over the heads up to rounding."""
+    B, H, H_kv, N, d = 1, 32, 1, 16384, 128
+    say("bwd multi-query full size vs copied heads")
+    q, k, v, do = si.make_qkv_dout_shared(B, H, H_kv, N, d, "bf16", 9950)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = grads(q, k, v, do, scale, "causal", 0)
+    kc, vc = (t.repeat_interleave(H, dim=1).contiguous() for t in (k, v))
+    cq, ck, cv = grads(q, kc, vc, do, scale, "causal", 0)
+    assert torch.equal(dq, cq)
+    sk = ck.float().sum(dim=1, keepdim=True).double().cpu().numpy()
+    sv = cv.float().sum(dim=1, keepdim=True).double().cpu().numpy()
+    check(dk, sk, "bf16", "dk vs copies")
+    check(dv, sv, "bf16", "dv vs copies")
+
+
 def test_bwd_shared_heads_full_size_sampled():
     """B=1 H=32 H_kv=8 N=16384 d=128 bf16 causal: sampled query rows (dq) of
     two query heads and sampled keys (dk, dv summed over the four query
