@@ -419,20 +419,13 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
       constexpr bool MASKED = decltype(masked)::value;
       const FA_AS3 unsigned char* qc = qbuf(s);
       const FA_AS3 unsigned char* oc = obuf(s);
-      // S = Q K^T and dP - D = dO V^T - D (rows x keys); s[qb][r] is row
+      // S = Q K^T and dP = dO V^T (rows x keys); s[qb][r] is row
       // qt*64 + 32qb + 8(r/4) + 4half + r%4 and key kj
       fa_f32x16 sc[NQB], dp[NQB];
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const fa_f32x4 dv4 = *(const FA_AS3 fa_f32x4*)&dl[s][32 * qb + 8 * a + 4 * half];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sc[qb][4 * a + e] = 0.f;
-            dp[qb][4 * a + e] = -dv4[e];
-          }
-        }
+        for (int r = 0; r < 16; ++r) sc[qb][r] = dp[qb][r] = 0.f;
 #pragma unroll
       for (int sl = 0; sl < NQF; ++sl)
 #pragma unroll
@@ -450,6 +443,7 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const fa_f32x4 l4 = *(const FA_AS3 fa_f32x4*)&ls[s][32 * qb + 8 * a + 4 * half];
+          const fa_f32x4 d4 = *(const FA_AS3 fa_f32x4*)&dl[s][32 * qb + 8 * a + 4 * half];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * a + e;
@@ -457,7 +451,7 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
             float pv = exp2_hw(__builtin_fmaf(sc[qb][r], c2, -l4[e] * LOG2E));
             if (MASKED && !visible(i, kj, N, p.mask_kind, p.window)) pv = 0.f;
             pr[r] = pv;
-            ds[r] = pv * dp[qb][r];
+            ds[r] = pv * (dp[qb][r] - d4[e]);
           }
         }
         pf[qb][0] = pack8<DT>(&pr[0]);
