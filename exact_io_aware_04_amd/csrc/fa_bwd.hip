@@ -9,13 +9,18 @@
 // one number), so no N x N matrix is read or written.  With
 //   dP = do v^T,  D_i = sum_j P_ij dP_ij = <do_i, o_i>,  dS = P (dP - D):
 //   dq = scale dS k,   dk = scale dS^T q,   dv = P^T do.
-// Three kernels, launched in this order on one stream:
-//   fa_bwd_delta_kernel  D_i = <do_i, o_i> in fp32, one pass over do and o
-//   fa_bwd_dq_kernel     per 256-row query tile, over its key blocks:
-//                        S^T, dP^T, dS^T, dq^T += k^T dS^T   (lane = query)
-//   fa_bwd_dkdv_kernel   per 128-key tile, over its query blocks (of every
-//                        query head that shares the key/value head):
-//                        S, dP, dS, dv^T += do^T P, dk^T += q^T dS (lane = key)
+// Kernels, launched in this order on one stream:
+//   fa_bwd_delta_kernel   D_i = <do_i, o_i> in fp32, one pass over do and o
+//   fa_bwd_dkdv_kernel    per 128-key tile, over its query blocks (of the
+//                         query heads that share the key/value head, or of
+//                         one part of them): S, dP, dS, dv^T += do^T P,
+//                         dk^T += q^T dS (lane = key)
+//   fa_bwd_combine_kernel only when a tile's query heads are split over
+//                         several workgroups: adds their fp32 partials,
+//                         which sit in dq's memory
+//   fa_bwd_dq_kernel      per 256-row query tile, over its key blocks:
+//                         S^T, dP^T, dS^T, dq^T += k^T dS^T (lane = query);
+//                         last, since it overwrites that memory
 // S and dP are formed in both loop kernels (seven matrix products per
 // query-block / key-block pair instead of five), so that no partial dq is
 // accumulated across workgroups.
