@@ -404,17 +404,24 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
   // query block qt -> slot b: q and do rows, and lse and D of its 64 rows
   // (one 4-byte load per lane by waves 0 and 1).  Rows past N read as zeros
   // and contribute nothing below, since their q and do rows are zero.
+  // lse arrives in a register of wave 0 (lane = row; rows past N read 0)
+  // and is stored to LDS as -lse log2 e by put_lse before the barrier that
+  // ends the step, so the exponent below is one FMA per score
+  float lse_next = 0.f;
   auto load = [&](int qt, int b) {
     load_block<D, BW>(Qh, qt * BB, N, loff, qbuf(b), wave);
     load_block<D, BW>(dOh, qt * BB, N, loff, obuf(b), wave);
-    if (wave < 2) {
-      const int r0 = qt * BB;
-      const float* src = (wave == 0 ? lse_h : dl_h) + (r0 < N ? r0 : 0);
+    const int r0 = qt * BB;
+    if (wave == 0) {
+      lse_next = r0 + lane < N ? lse_h[r0 + lane] : 0.f;
+    } else if (wave == 1) {
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)src, 0, max(min(N - r0, BB), 0) * 4, FA_BUF_WORD3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (FA_AS3 void*)(wave == 0 ? &ls[b][0] : &dl[b][0]), 4, lane * 4, 0, 0, 0);
+          (void*)(dl_h + (r0 < N ? r0 : 0)), 0, max(min(N - r0, BB), 0) * 4, FA_BUF_WORD3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_AS3 void*)&dl[b][0], 4, lane * 4, 0, 0, 0);
     }
+  };
+  auto put_lse = [&](int b) {
+    if (wave == 0) ls[b][lane] = -lse_next * LOG2E;
   };
   auto step = [&](int qt, int s) {
     if (qt + 1 < qhi) load(qt + 1, s ^ 1);
@@ -453,7 +460,7 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * a + e;
             const int i = qt * BB + 32 * qb + 8 * a + 4 * half + e;
-            float pv = exp2_hw(__builtin_fmaf(sc[qb][r], c2, -l4[e] * LOG2E));
+            float pv = exp2_hw(__builtin_fmaf(sc[qb][r], c2, l4[e]));
             if (MASKED && !visible(i, kj, N, p.mask_kind, p.window)) pv = 0.f;
             pr[r] = pv;
             ds[r] = pv * (dp[qb][r] - d4[e]);
@@ -497,6 +504,7 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
       compute(std::true_type{});
     else if (cls == FA_TILE_FULL)
       compute(std::false_type{});
+    if (qt + 1 < qhi) put_lse(s ^ 1);
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
     barrier_nofence();
   };
@@ -510,6 +518,7 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
     lse_h = p.lse + (size_t)bh * N;
     dl_h = p.delta + (size_t)bh * N;
     load(qlo, 0);
+    put_lse(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int qt = qlo;;) {
