@@ -36,8 +36,6 @@
 // both without bank conflicts (see bswz).
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
-
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "tile_class.h"
@@ -61,13 +59,6 @@ constexpr float LOG2E = 1.44269504088896340736f;
 template <int D>
 __device__ __forceinline__ int bswz(int r) {
   return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-}
-
-// Visibility of key j to query i (the predicate of the forward pass).
-__device__ __forceinline__ bool visible(int i, int j, int N, int mask_kind, int window) {
-  if (j >= N) return false;
-  if (mask_kind == FA_MASKK_NONE) return true;
-  return j <= i && (mask_kind == FA_MASKK_CAUSAL || j > i - window);
 }
 
 // Query-block range [lo, hi) (blocks of bq rows) holding every query that
@@ -279,10 +270,7 @@ fa_bwd_dq_kernel(FaBwdParams p) {
       load_block<D, BWQ>(Vh, (kt + 1) * BB, N, loff, vbuf(s ^ 1), wave);
     }
     const int cls = fa_classify(qb0, qb1, kt * BB, BB, N, p.mask_kind, p.window);
-    // one body per block class, so the (wave-uniform) class is tested once per
-    // block rather than once per score
-    auto compute = [&](auto masked) {
-      constexpr bool MASKED = decltype(masked)::value;
+    if (cls != FA_TILE_SKIP) {
       const FA_AS3 unsigned char* kc = kbuf(s);
       const FA_AS3 unsigned char* vc = vbuf(s);
       // S^T = K Q^T and dP^T - D = V dO^T - D (keys x rows)
@@ -305,17 +293,32 @@ fa_bwd_dq_kernel(FaBwdParams p) {
         }
       // P^T = 2^(s c2 - lse log2 e), 0 where masked; dS^T = P^T (dP^T - D)
       // (s[kb][r] is key kt*64 + 32kb + 8(r/4) + 4half + r%4 of row qi)
+      // (boundary blocks: one wave-uniform branch around the mask, so the
+      // dq accumulators see one code path)
+      float pr[NKB][16];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pr[kb][r] = exp2_hw(__builtin_fmaf(sc[kb][r], c2, -lse2));
+      if (cls == FA_TILE_PARTIAL) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = kt * BB + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+            // visible under the mask (bitwise operators: no branches)
+            const bool vis = (j < N) & ((p.mask_kind == FA_MASKK_NONE) |
+                                        ((j <= qi) & ((p.mask_kind == FA_MASKK_CAUSAL) |
+                                                      (j > qi - p.window))));
+            pr[kb][r] = vis ? pr[kb][r] : 0.f;
+          }
+      }
       fa_u32x4 dsf[NKB][2];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         float ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kt * BB + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          float pr = exp2_hw(__builtin_fmaf(sc[kb][r], c2, -lse2));
-          if (MASKED && !visible(qi, j, N, p.mask_kind, p.window)) pr = 0.f;
-          ds[r] = pr * dp[kb][r];
-        }
+        for (int r = 0; r < 16; ++r) ds[r] = pr[kb][r] * dp[kb][r];
         dsf[kb][0] = pack8<DT>(&ds[0]);
         dsf[kb][1] = pack8<DT>(&ds[8]);
       }
@@ -329,11 +332,7 @@ fa_bwd_dq_kernel(FaBwdParams p) {
             const FA_AS3 unsigned char* blk = kc + (32 * kb + 16 * t) * ROWB;
             acc[cb] = mma16<DT>(tr_operand(blk, rd.trlo[cb], rd.trhi[cb]), dsf[kb][t], acc[cb]);
           }
-    };
-    if (cls == FA_TILE_PARTIAL)
-      compute(std::true_type{});
-    else if (cls == FA_TILE_FULL)
-      compute(std::false_type{});
+    }
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
     barrier_nofence();
   };
@@ -426,9 +425,7 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
   auto step = [&](int qt, int s) {
     if (qt + 1 < qhi) load(qt + 1, s ^ 1);
     const int cls = fa_classify(qt * BB, min(qt * BB + BB, N), kw0, BR, N, p.mask_kind, p.window);
-    // one body per block class (see the dq kernel)
-    auto compute = [&](auto masked) {
-      constexpr bool MASKED = decltype(masked)::value;
+    if (cls != FA_TILE_SKIP) {
       const FA_AS3 unsigned char* qc = qbuf(s);
       const FA_AS3 unsigned char* oc = obuf(s);
       // S = Q K^T and dP = dO V^T (rows x keys); s[qb][r] is row
@@ -447,27 +444,47 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
           sc[qb] = mma16<DT>(qa, kf[sl], sc[qb]);
           dp[qb] = mma16<DT>(oa, vf[sl], dp[qb]);
         }
-      // P = 2^(s c2 - lse log2 e) (0 where masked), dS = P (dP - D)
-      fa_u32x4 pf[NQB][2], dsf[NQB][2];
+      // P = 2^(s c2 - lse log2 e), 0 where masked: boundary blocks take one
+      // (wave-uniform) branch around the mask of all 64 rows, which leaves
+      // the gradient accumulators untouched (one code path for them, so the
+      // register allocator keeps them in place)
+      float pr[NQB][16];
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        float pr[16], ds[16];
+      for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const fa_f32x4 l4 = *(const FA_AS3 fa_f32x4*)&ls[s][32 * qb + 8 * a + 4 * half];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pr[qb][4 * a + e] = exp2_hw(__builtin_fmaf(sc[qb][4 * a + e], c2, l4[e]));
+        }
+      if (cls == FA_TILE_PARTIAL) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = qt * BB + 32 * qb + 8 * (r >> 2) + 4 * half + (r & 3);
+            // visible under the mask (bitwise operators: no branches)
+            const bool vis = (kj < N) & ((p.mask_kind == FA_MASKK_NONE) |
+                                         ((kj <= i) & ((p.mask_kind == FA_MASKK_CAUSAL) |
+                                                       (kj > i - p.window))));
+            pr[qb][r] = vis ? pr[qb][r] : 0.f;
+          }
+      }
+      // dS = P (dP - D)
+      fa_u32x4 pf[NQB][2], dsf[NQB][2];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float ds[16];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
           const fa_f32x4 d4 = *(const FA_AS3 fa_f32x4*)&dl[s][32 * qb + 8 * a + 4 * half];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * a + e;
-            const int i = qt * BB + 32 * qb + 8 * a + 4 * half + e;
-            float pv = exp2_hw(__builtin_fmaf(sc[qb][r], c2, l4[e]));
-            if (MASKED && !visible(i, kj, N, p.mask_kind, p.window)) pv = 0.f;
-            pr[r] = pv;
-            ds[r] = pv * (dp[qb][r] - d4[e]);
-          }
+          for (int e = 0; e < 4; ++e)
+            ds[4 * a + e] = pr[qb][4 * a + e] * (dp[qb][4 * a + e] - d4[e]);
         }
-        pf[qb][0] = pack8<DT>(&pr[0]);
-        pf[qb][1] = pack8<DT>(&pr[8]);
+        pf[qb][0] = pack8<DT>(&pr[qb][0]);
+        pf[qb][1] = pack8<DT>(&pr[qb][8]);
         dsf[qb][0] = pack8<DT>(&ds[0]);
         dsf[qb][1] = pack8<DT>(&ds[8]);
       }
@@ -499,11 +516,7 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
           if (i >= R) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
       }
-    };
-    if (cls == FA_TILE_PARTIAL)
-      compute(std::true_type{});
-    else if (cls == FA_TILE_FULL)
-      compute(std::false_type{});
+    }
     if (qt + 1 < qhi) put_lse(s ^ 1);
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
     barrier_nofence();
