@@ -354,7 +354,7 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
   constexpr int NQB = BB / 32, NCB = D / 32, NQF = D / 16, ROWB = 2 * D, TILEB = BB * ROWB;
   __shared__ __attribute__((aligned(1024))) unsigned char qs0[TILEB], qs1[TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char os0[TILEB], os1[TILEB];
-  __shared__ __attribute__((aligned(256))) float ls[2][BB], dl[2][BB];  // lse, D
+  __shared__ __attribute__((aligned(256))) float ls[2][BB], dl[2][BB];  // -lse log2 e, D
   auto qbuf = [&](int b) { return (FA_AS3 unsigned char*)(b == 0 ? qs0 : qs1); };
   auto obuf = [&](int b) { return (FA_AS3 unsigned char*)(b == 0 ? os0 : os1); };
 
@@ -402,8 +402,8 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
 
   // query block qt -> slot b: q and do rows, and lse and D of its 64 rows
   // (one 4-byte load per lane by waves 0 and 1).  Rows past N read as zeros
-  // and contribute nothing below, since their q and do rows are zero.
-  // lse arrives in a register of wave 0 (lane = row; rows past N read 0)
+  // and contribute nothing below, since their q and do rows are zero.  D
+  // goes to LDS by DMA; lse arrives in a register of wave 0 (lane = row)
   // and is stored to LDS as -lse log2 e by put_lse before the barrier that
   // ends the step, so the exponent below is one FMA per score
   float lse_next = 0.f;
