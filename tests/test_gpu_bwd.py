@@ -184,24 +184,24 @@ def test_bwd_shared_heads_match_copied_heads(H, H_kv):
 
 # Groups of 8 or more query heads per key/value head with few key tiles: the
 # dk/dv pass splits each tile's query heads over kv_parts workgroups (at most
-# g / 4) and sums their fp32 partials.  (H, H_kv, N): parts 8 (g = 32, N =
-# 1000), 2 uneven (g = 9: heads 0-3 and 4-8), 2 (g = 8 with two key/value
-# heads), 3 (g = 12).
-SPLIT_HEADS = [(32, 1, 1000), (9, 1, 333), (16, 2, 700), (12, 1, 129)]
+# g / 4) and sums their fp32 partials.  (B, H, H_kv, N): parts 8 (g = 32,
+# N = 1000), 2 uneven (g = 9: heads 0-3 and 4-8), 2 (g = 8 with two
+# key/value heads), 3 (g = 12), 4 with two batch entries (g = 16).
+SPLIT_HEADS = [(1, 32, 1, 1000), (1, 9, 1, 333), (1, 16, 2, 700), (1, 12, 1, 129), (2, 16, 1, 300)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 100)])
 def test_bwd_split_query_heads_against_oracle(dtype, d, mask, window):
-    for H, H_kv, N in SPLIT_HEADS:
-        say("bwd split query heads", dtype, d, mask, window, H, H_kv, N)
-        q, k, v, do = si.make_qkv_dout_shared(1, H, H_kv, N, d, dtype, 9750 + N + d + H)
+    for B, H, H_kv, N in SPLIT_HEADS:
+        say("bwd split query heads", dtype, d, mask, window, B, H, H_kv, N)
+        q, k, v, do = si.make_qkv_dout_shared(B, H, H_kv, N, d, dtype, 9750 + N + d + H)
         scale = 1.0 / math.sqrt(d)
         dq, dk, dv = grads(q, k, v, do, scale, mask, window)
         rq, rk, rv = oracle.attention_bwd_gqa(q, k, v, do, scale, mask, window)
         for nm, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-            check(g, r, dtype, "%s H=%d H_kv=%d N=%d" % (nm, H, H_kv, N))
+            check(g, r, dtype, "%s B=%d H=%d H_kv=%d N=%d" % (nm, B, H, H_kv, N))
 
 
 def test_bwd_multi_query_full_size_matches_copied_heads():
