@@ -69,6 +69,8 @@ def load():
     lib.fa_fwd_record_tiles.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, vp, vp]
     lib.fa_fwd_record_tiles.restype = i
     lib.fa_tile_shape.argtypes = [i, i, ip, ip, ip]
+    lib.fa_bwd_kv_parts.restype = i
+    lib.fa_bwd_kv_parts.argtypes = [i, i, i, i, i, ip]
     lib.fa_tile_shape.restype = i
     lib.fa_tile_map.argtypes = [i, i, i, i, i, vp]
     lib.fa_tile_map.restype = i
@@ -136,6 +138,15 @@ def fa_fwd_record_tiles(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window,
                         in_dtype, out_dtype, tiles, stream) -> int:
     return load().fa_fwd_record_tiles(q, k, v, o, lse, B, H, N, d, scale, mask_kind,
                                       window, in_dtype, out_dtype, tiles, stream)
+
+
+def fa_bwd_kv_parts(B: int, H: int, H_kv: int, N: int, compute_units: int) -> int:
+    """Workgroups per key tile of the backward's dk/dv pass; raises on error."""
+    parts = ctypes.c_int()
+    st = load().fa_bwd_kv_parts(B, H, H_kv, N, compute_units, ctypes.byref(parts))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_kv_parts")
+    return parts.value
 
 
 def fa_tile_shape(d: int, in_dtype: int):

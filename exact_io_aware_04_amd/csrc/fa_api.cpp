@@ -360,6 +360,21 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
   return ok();
 }
 
+// Few key/value heads leave the dk/dv pass with few workgroups (one per
+// key/value head and 128-key tile), each running all g = H / H_kv query
+// heads.  Then the query heads are split over kv_parts workgroups per tile
+// (aiming at four workgroups per compute unit), whose fp32 partial sums go
+// to dq's memory -- free until the dq pass, which runs last -- and are added
+// by a small kernel.  The partials take 8 kv_parts B H_kv N d bytes of dq's
+// 2 B H N d, hence kv_parts <= g / 4.  (Arguments already validated.)
+static int bwd_kv_parts(int B, int H, int H_kv, int N, int cus) {
+  const long long tiles = (long long)B * H_kv * ((N + FA_BWD_WAVES * 32 - 1) / (FA_BWD_WAVES * 32));
+  const long long want = 4LL * cus;
+  const int cap = (H / H_kv) / 4;
+  if (cap < 2 || tiles >= want) return 1;
+  return (int)std::min<long long>(cap, (want + tiles - 1) / tiles);
+}
+
 int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
                int H_kv, int N, int d, float scale, int mask_kind, int window, int dtype,
@@ -393,22 +408,8 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const
   p.n_q_tiles = (N + FA_BWD_DQ_WAVES * 32 - 1) / (FA_BWD_DQ_WAVES * 32);
   p.n_k_tiles = (N + FA_BWD_WAVES * 32 - 1) / (FA_BWD_WAVES * 32);
   p.heavy_first = mask_kind != FA_MASK_NONE ? 1 : 0;
-  // Few key/value heads leave the dk/dv pass with few workgroups (one per
-  // key/value head and 128-key tile), each running all g = H / H_kv query
-  // heads.  Then the query heads are split over kv_parts workgroups per tile
-  // (aiming at four workgroups per compute unit), whose fp32 partial sums
-  // go to dq's memory -- free until the dq pass, which runs last -- and are
-  // added by a small kernel.  The partials take 8 kv_parts B H_kv N d bytes
-  // of dq's 2 B H N d, hence kv_parts <= g / 4.
-  {
-    const long long wgs = (long long)B * H_kv * p.n_k_tiles;
-    const long long want = 4LL * device_cus();
-    const int cap = p.kv_group / 4;
-    int parts = 1;
-    if (cap >= 2 && wgs < want) parts = (int)std::min<long long>(cap, (want + wgs - 1) / wgs);
-    p.kv_parts = parts;
-    p.part_scratch = parts > 1 ? (float*)dq : nullptr;
-  }
+  p.kv_parts = bwd_kv_parts(B, H, H_kv, N, device_cus());
+  p.part_scratch = p.kv_parts > 1 ? (float*)dq : nullptr;
   hipError_t e = fa_launch_bwd(dtype, d, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
@@ -456,6 +457,16 @@ int fa_fwd_record_tiles(const void* q, const void* k, const void* v, void* o, fl
     return fail(FA_ERR_INVALID_ARG, "E4M3 inputs go through fa_fwd_fp8");
   return run_fwd(q, k, v, o, lse, B, H, H, N, d, scale, 1.f, mask_kind, window, in_dtype,
                  out_dtype, tiles, stream);
+}
+
+int fa_bwd_kv_parts(int B, int H, int H_kv, int N, int compute_units, int* parts) {
+  if (!parts) return fail(FA_ERR_INVALID_ARG, "null pointer argument");
+  if (B < 1 || H < 1 || N < 1 || compute_units < 1)
+    return fail(FA_ERR_INVALID_ARG, "B, H, N and compute_units must be >= 1");
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0)
+    return fail(FA_ERR_INVALID_ARG, "H_kv must divide H = %d (got %d)", H, H_kv);
+  *parts = bwd_kv_parts(B, H, H_kv, N, compute_units);
+  return ok();
 }
 
 int fa_tile_shape(int d, int in_dtype, int* rows_per_workgroup, int* rows_per_wave,

@@ -246,6 +246,18 @@ int fa_fwd_record_tiles(const void* q, const void* k, const void* v, void* o,
                         unsigned char* tiles, void* stream);
 
 /*
+ * Split of the backward's dk/dv pass that fa_bwd_gqa chooses on a device
+ * with `compute_units` compute units: *parts receives the number of
+ * workgroups each 128-key tile's query heads are divided over (1: no split).
+ * The split is taken when a group has g = H / H_kv >= 8 query heads and the
+ * B * H_kv * ceil(N / 128) tiles give fewer than four workgroups per compute
+ * unit; then parts = min(g / 4, ceil(4 * compute_units / tiles)).  Host
+ * only; no device call.  FA_ERR_INVALID_ARG for B, H, N, compute_units < 1,
+ * an H_kv that does not divide H, or a null `parts`.
+ */
+int fa_bwd_kv_parts(int B, int H, int H_kv, int N, int compute_units, int* parts);
+
+/*
  * Tile geometry the dispatcher uses for (d, in_dtype): rows handled by one
  * workgroup, rows handled by one wavefront (the granularity at which work is
  * skipped), and keys per K/V block.  Host only; no device call.

@@ -29,7 +29,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = fa.load()
     names = fa.declared_functions()
     assert {"fa_fwd", "fa_fwd_gqa", "fa_fwd_fp8", "fa_bwd", "fa_decode", "fa_decode_workspace_bytes", "fa_fwd_record_tiles", "fa_tile_shape", "fa_tile_map",
-            "fa_status_string", "fa_last_error", "fa_probe_mfma", "fa_mfma_ceiling"} <= set(names)
+            "fa_status_string", "fa_last_error", "fa_probe_mfma", "fa_mfma_ceiling",
+            "fa_bwd_kv_parts"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     # and they really are C symbols of the shared object
@@ -359,3 +360,28 @@ def test_bwd_gqa_overlap_checks_use_the_key_value_head_count():
     assert call_bwd_gqa(dv=DK + kvbytes - 16) == fa.FA_ERR_INVALID_ARG
     assert call_bwd_gqa(H_kv=8) in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
     assert call_bwd_gqa(H_kv=1) in (fa.FA_ERR_NO_DEVICE, fa.FA_ERR_HIP)
+
+
+def test_bwd_kv_parts_planner():
+    """The backward's dk/dv split (host only): split when a group has at least
+    8 query heads and the tiles give fewer than 4 workgroups per compute
+    unit; parts = min(g / 4, ceil(4 CUs / tiles)), tiles = B H_kv ceil(N / 128)."""
+    P = fa.fa_bwd_kv_parts
+    # the benchmarked shapes on 256 compute units
+    assert P(1, 32, 32, 16384, 256) == 1      # plain heads: g = 1
+    assert P(1, 32, 8, 16384, 256) == 1       # g = 4: no room in dq for partials
+    assert P(1, 32, 1, 16384, 256) == 8       # multi-query: 128 tiles, capped at g / 4
+    # the GPU test shapes
+    assert P(1, 32, 1, 1000, 256) == 8
+    assert P(1, 9, 1, 333, 256) == 2
+    assert P(1, 16, 2, 700, 256) == 2
+    assert P(1, 12, 1, 129, 256) == 3
+    assert P(2, 16, 1, 300, 256) == 4
+    assert P(1, 8, 1, 600, 256) == 2
+    # enough tiles already: no split; fewer compute units: fewer parts
+    assert P(8, 32, 1, 16384, 256) == 1       # 1024 tiles = 4 per compute unit
+    assert P(1, 32, 1, 16384, 64) == 2        # ceil(256 / 128)
+    assert P(1, 32, 1, 16384, 1000) == 8
+    for bad in ((0, 32, 1, 16, 256), (1, 32, 3, 16, 256), (1, 32, 1, 0, 256), (1, 32, 1, 16, 0)):
+        with pytest.raises(fa.FaError):
+            P(*bad)
