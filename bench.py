@@ -619,7 +619,8 @@ def main():
             " cast to E4M3, bf16 output" if fp8 else "", w.seed),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "N": w.N, "d": w.d,
                    "mask": w.mask, "window": w.window, "scale": w.scale,
-                   "flops_per_step": flops, "pct_of_peak": round(100 * value / peak, 2)},
+                   "flops_per_step": flops, "pct_of_peak": round(100 * value / peak, 2),
+                   "inputs_sha256": {"q": si.sha256(q), "k": si.sha256(k), "v": si.sha256(v)}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": load_traffic(w),

@@ -246,6 +246,17 @@ DecodePlan decode_plan(int B, int H_kv, int Nq, int Nk, int mask_kind, int windo
   return pl;
 }
 
+// Most chunks any mask can give for these sizes.  decode_plan's chunk count
+// is ceil(n / ceil(n / want)) <= want = min(n, cap) for n blocks, and a mask
+// only removes blocks, so min(unmasked blocks, cap) bounds every mask and
+// window (the count itself is not monotone in n: 33 blocks with cap 32 give
+// 17 chunks, 32 blocks give 32).
+int decode_max_chunks(int B, int H_kv, int Nk) {
+  const long long n = (Nk + FA_DECODE_KEYS - 1) / FA_DECODE_KEYS;
+  const long long pairs = (long long)B * H_kv;
+  return (int)std::max(1LL, std::min({n, (2048 + pairs - 1) / pairs, 256LL}));
+}
+
 long long decode_ws_bytes(int B, int H, int Nq, int d, int n_chunks) {
   return (long long)n_chunks * B * H * Nq * (d + 1) * (long long)sizeof(float);
 }
@@ -301,9 +312,8 @@ long long fa_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int 
     fail(FA_ERR_INVALID_ARG, "invalid sizes");
     return -1;
   }
-  const DecodePlan pl = decode_plan(B, H_kv, Nq, Nk, FA_MASK_NONE, 0);
   ok();
-  return decode_ws_bytes(B, H, Nq, d, pl.n_chunks);
+  return decode_ws_bytes(B, H, Nq, d, decode_max_chunks(B, H_kv, Nk));
 }
 
 int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -368,7 +378,8 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
 // by a small kernel.  The partials take 8 kv_parts B H_kv N d bytes of dq's
 // 2 B H N d, hence kv_parts <= g / 4.  (Arguments already validated.)
 static int bwd_kv_parts(int B, int H, int H_kv, int N, int cus) {
-  const long long tiles = (long long)B * H_kv * ((N + FA_BWD_WAVES * 32 - 1) / (FA_BWD_WAVES * 32));
+  const long long tiles =
+      (long long)B * H_kv * (((long long)N + FA_BWD_WAVES * 32 - 1) / (FA_BWD_WAVES * 32));
   const long long want = 4LL * cus;
   const int cap = (H / H_kv) / 4;
   if (cap < 2 || tiles >= want) return 1;
@@ -463,6 +474,7 @@ int fa_bwd_kv_parts(int B, int H, int H_kv, int N, int compute_units, int* parts
   if (!parts) return fail(FA_ERR_INVALID_ARG, "null pointer argument");
   if (B < 1 || H < 1 || N < 1 || compute_units < 1)
     return fail(FA_ERR_INVALID_ARG, "B, H, N and compute_units must be >= 1");
+  if (N >= (1 << 30)) return fail(FA_ERR_INVALID_ARG, "N must be < 2^30");
   if (H_kv < 1 || H_kv > H || H % H_kv != 0)
     return fail(FA_ERR_INVALID_ARG, "H_kv must divide H = %d (got %d)", H, H_kv);
   *parts = bwd_kv_parts(B, H, H_kv, N, compute_units);

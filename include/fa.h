@@ -160,7 +160,9 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
  *   d          64 or 128;  dtype FA_DTYPE_F16 or FA_DTYPE_BF16
  *   workspace  device memory of at least fa_decode_workspace_bytes(...)
  *              bytes, 16-byte aligned, overlapping no other argument; its
- *              contents on entry do not matter and are left undefined
+ *              contents on entry do not matter and are left undefined.
+ *              fa_decode_workspace_bytes bounds every mask_kind and window
+ *              for the sizes given (-1 for invalid sizes)
  * Other arguments, arithmetic and errors as for fa_fwd.
  */
 long long fa_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d);
@@ -253,7 +255,7 @@ int fa_fwd_record_tiles(const void* q, const void* k, const void* v, void* o,
  * B * H_kv * ceil(N / 128) tiles give fewer than four workgroups per compute
  * unit; then parts = min(g / 4, ceil(4 * compute_units / tiles)).  Host
  * only; no device call.  FA_ERR_INVALID_ARG for B, H, N, compute_units < 1,
- * an H_kv that does not divide H, or a null `parts`.
+ * N >= 2^30, an H_kv that does not divide H, or a null `parts`.
  */
 int fa_bwd_kv_parts(int B, int H, int H_kv, int N, int compute_units, int* parts);
 

@@ -235,6 +235,46 @@ def test_decode_workspace_bytes():
     assert fa.fa_decode_workspace_bytes(1, 4, 4, 9, 8, 64) == -1     # Nq > Nk
 
 
+@pytest.mark.parametrize("B,H,H_kv,Nq", [(8, 32, 8, 1), (1, 8, 2, 4), (64, 8, 1, 1), (2, 32, 32, 1)])
+def test_decode_workspace_bound_holds_for_every_mask(B, H, H_kv, Nq):
+    """fa_decode_workspace_bytes must cover every mask and window: the chunk
+    count of the split is not monotone in the number of key blocks, so a
+    sliding window (fewer blocks) can need more chunks than no mask.  The
+    workspace check runs on the host before any device call, so a call with
+    exactly the documented size gets past it (NO_DEVICE here, never
+    INVALID_ARG).  Cache sizes straddle multiples of the chunk target."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    pairs = B * H_kv
+    target = min(-(-2048 // pairs), 256)
+    d, dt = 128, fa.FA_DTYPE_BF16
+    for m in (1, 2, 3):
+        for Nk in {32 * target * m - 32, 32 * target * m - 1, 32 * target * m, 32 * target * m + 1,
+                   32 * target * m + 32, 32 * target * m + 33}:
+            if Nk < Nq:
+                continue
+            ws = fa.fa_decode_workspace_bytes(B, H, H_kv, Nq, Nk, d)
+            assert ws > 0
+            nq = B * H * Nq * d * 2
+            nkv = B * H_kv * Nk * d * 2
+            # dummy, aligned, non-overlapping device-address stand-ins
+            base = 1 << 40
+            qp, kp = base, base + (1 << 36)
+            vp, op = kp + (1 << 36), kp + (2 << 36)
+            lp, wp = kp + (3 << 36), kp + (4 << 36)
+            assert nq < (1 << 36) and nkv < (1 << 36) and ws < (1 << 36)
+            windows = [None, 1, 31, 32, 33, 1000, Nk - 33, Nk - 32, Nk - 1, Nk, Nk + 5]
+            for w in windows:
+                mask = fa.FA_MASK_CAUSAL if w is None else fa.FA_MASK_SLIDING
+                if w is not None and w < 1:
+                    continue
+                for mk in ((mask,) if w is not None else (fa.FA_MASK_NONE, fa.FA_MASK_CAUSAL)):
+                    st = fa.fa_decode(qp, kp, vp, op, lp, B, H, H_kv, Nq, Nk, d, 0.1, mk,
+                                      w or 0, dt, wp, ws, None)
+                    assert st == fa.FA_ERR_NO_DEVICE, (Nk, w, mk, fa.fa_last_error())
+
+
 def call_decode(**kw):
     args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=8, H_kv=2, Nq=1, Nk=1000, d=128, scale=0.1,
                 mask_kind=fa.FA_MASK_CAUSAL, window=0, dtype=fa.FA_DTYPE_BF16, ws=DQ,
@@ -382,6 +422,9 @@ def test_bwd_kv_parts_planner():
     assert P(8, 32, 1, 16384, 256) == 1       # 1024 tiles = 4 per compute unit
     assert P(1, 32, 1, 16384, 64) == 2        # ceil(256 / 128)
     assert P(1, 32, 1, 16384, 1000) == 8
-    for bad in ((0, 32, 1, 16, 256), (1, 32, 3, 16, 256), (1, 32, 1, 0, 256), (1, 32, 1, 16, 0)):
+    for bad in ((0, 32, 1, 16, 256), (1, 32, 3, 16, 256), (1, 32, 1, 0, 256), (1, 32, 1, 16, 0),
+                (1, 32, 1, 1 << 30, 256), (1, 32, 1, 2**31 - 1, 256)):
         with pytest.raises(fa.FaError):
             P(*bad)
+    # the largest accepted N still plans a positive split
+    assert P(1, 32, 1, (1 << 30) - 1, 256) == 1
