@@ -2,7 +2,7 @@
 gfx950 (MI355X).
 
 The functions named like the C ABI (``fa_fwd``, ``fa_fwd_gqa``, ``fa_fwd_fp8``, ``fa_bwd_gqa``, ``fa_decode``,
-``fa_decode_workspace_bytes``, ``fa_bwd``, ``fa_fwd_record_tiles``,
+``fa_decode_workspace_bytes``, ``fa_decode_noalloc``, ``fa_bwd``, ``fa_fwd_record_tiles``,
 ``fa_tile_shape``, ``fa_tile_map``, ``fa_status_string``, ``fa_last_error``,
 ``fa_probe_mfma``, ``fa_mfma_ceiling``) only marshal arguments: pointers are plain integers
 (device addresses, e.g. ``tensor.data_ptr()``), the stream is a hipStream_t
@@ -66,6 +66,8 @@ def load():
     lib.fa_decode_workspace_bytes.restype = ctypes.c_longlong
     lib.fa_decode.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, i, vp, ctypes.c_longlong, vp]
     lib.fa_decode.restype = i
+    lib.fa_decode_noalloc.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, i, vp]
+    lib.fa_decode_noalloc.restype = i
     lib.fa_fwd_record_tiles.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, vp, vp]
     lib.fa_fwd_record_tiles.restype = i
     lib.fa_tile_shape.argtypes = [i, i, ip, ip, ip]
@@ -132,6 +134,12 @@ def fa_decode(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, mask_kind, window, 
               workspace, workspace_bytes, stream) -> int:
     return load().fa_decode(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, mask_kind, window,
                             dtype, workspace, workspace_bytes, stream)
+
+
+def fa_decode_noalloc(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, mask_kind, window, dtype,
+                      stream) -> int:
+    return load().fa_decode_noalloc(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, mask_kind,
+                                    window, dtype, stream)
 
 
 def fa_fwd_record_tiles(q, k, v, o, lse, B, H, N, d, scale, mask_kind, window,

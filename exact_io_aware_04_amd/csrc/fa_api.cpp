@@ -316,12 +316,15 @@ long long fa_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int 
   return decode_ws_bytes(B, H, Nq, d, decode_max_chunks(B, H_kv, Nk));
 }
 
-int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-              int H_kv, int Nq, int Nk, int d, float scale, int mask_kind, int window, int dtype,
-              void* workspace, long long workspace_bytes, void* stream) {
-  int st = check_decode_args(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, mask_kind, window,
-                             dtype);
-  if (st != FA_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// fa_decode after its argument check: workspace check, device check, launch.
+int run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int H_kv, int Nq, int Nk, int d, float scale, int mask_kind, int window,
+               int dtype, void* workspace, long long workspace_bytes, void* stream) {
+  int st;
   const int win = mask_kind == FA_MASK_SLIDING ? (window < Nk ? window : Nk) : 0;
   const DecodePlan pl = decode_plan(B, H_kv, Nq, Nk, mask_kind, win);
   const long long need = decode_ws_bytes(B, H, Nq, d, pl.n_chunks);
@@ -368,6 +371,42 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
   hipError_t e = fa_launch_decode(dtype, d, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int H_kv, int Nq, int Nk, int d, float scale, int mask_kind, int window, int dtype,
+              void* workspace, long long workspace_bytes, void* stream) {
+  const int st = check_decode_args(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, mask_kind,
+                                   window, dtype);
+  if (st != FA_OK) return st;
+  return run_decode(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, mask_kind, window, dtype,
+                    workspace, workspace_bytes, stream);
+}
+
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int H_kv, int Nq, int Nk, int d, float scale, int mask_kind,
+                      int window, int dtype, void* stream) {
+  int st = check_decode_args(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, mask_kind, window,
+                             dtype);
+  if (st != FA_OK) return st;
+  const int win = mask_kind == FA_MASK_SLIDING ? (window < Nk ? window : Nk) : 0;
+  const long long need = decode_ws_bytes(B, H, Nq, d, decode_plan(B, H_kv, Nq, Nk, mask_kind, win).n_chunks);
+  if (need > FA_DECODE_SCRATCH_BYTES)
+    return fail(FA_ERR_INVALID_ARG,
+                "these sizes need %lld bytes of chunk partials; the static scratch holds %lld",
+                need, (long long)FA_DECODE_SCRATCH_BYTES);
+  st = check_device();
+  if (st != FA_OK) return st;
+  void* scratch = nullptr;
+  const hipError_t e = fa_decode_scratch(&scratch);
+  if (e != hipSuccess)
+    return fail(FA_ERR_HIP, "address of the decode scratch: %s", hipGetErrorString(e));
+  return run_decode(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, mask_kind, window, dtype,
+                    scratch, FA_DECODE_SCRATCH_BYTES, stream);
 }
 
 // Few key/value heads leave the dk/dv pass with few workgroups (one per

@@ -24,6 +24,8 @@
 // in-lane plus one lane-half exchange.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "tile_class.h"
@@ -294,6 +296,37 @@ hipError_t launch_decode(const FaDecodeParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Chunk partials of fa_decode_noalloc: a file-scope device array instead of a
+// caller's workspace, for callers that cannot allocate.  Every GPU holds its
+// own copy at its own address; host code reaches it only through the address
+// hipGetSymbolAddress gives with that GPU current (the array's name is a
+// host-side stand-in, not a device address).  Calls that overlap on one GPU
+// share it and race.
+static __device__ __align__(256) float scratch[FA_DECODE_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];  // per device; nullptr until looked up
+}  // namespace
+
+hipError_t fa_decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t fa_launch_decode(int in_dtype, int d, const FaDecodeParams& p, hipStream_t stream) {
   if (in_dtype == 1) return d == 64 ? launch_decode<1, 64>(p, stream) : launch_decode<1, 128>(p, stream);

@@ -82,6 +82,13 @@ struct FaDecodeParams {
 };
 constexpr int FA_DECODE_KEYS = 32;
 constexpr int FA_DECODE_WAVES = 3;
+// Bytes of the file-scope device array that fa_decode_noalloc uses for the
+// chunk partials in place of a caller's workspace (8 MiB per GPU, held until
+// the process ends).
+constexpr long long FA_DECODE_SCRATCH_BYTES = 8LL << 20;
+// Device address of that array on the current device (looked up once per
+// device, with the device current, by hipGetSymbolAddress).
+hipError_t fa_decode_scratch(void** ptr);
 
 // Tile geometry.  Work is skipped per row block of 32 query rows (one
 // 32x32 matrix-core tile of rows); each wavefront owns one row block.

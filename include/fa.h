@@ -172,6 +172,23 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
               long long workspace_bytes, void* stream);
 
 /*
+ * fa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and arguments without the workspace.  The chunk partials
+ * go to a file-scope device array of 8 MiB (FA_DECODE_SCRATCH_BYTES) that
+ * every GPU the library runs on holds until the process ends.  The call
+ * allocates nothing.  Sizes whose partials need more than 8 MiB
+ * (fa_decode_workspace_bytes(...) > 8 MiB bounds them) return
+ * FA_ERR_INVALID_ARG before any device call.  All calls on one GPU share its
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller.  Other arguments, arithmetic and
+ * errors as for fa_decode.
+ */
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int H_kv, int Nq, int Nk, int d, float scale,
+                      int mask_kind, int window, int dtype, void* stream);
+
+/*
  * Backward pass of fa_fwd: the gradients dq, dk, dv of o with respect to q,
  * k and v for an output gradient dout (of a loss L: dout = dL/do).  With
  * P_ij the attention weights of fa_fwd (0 where masked):

@@ -428,3 +428,37 @@ def test_bwd_kv_parts_planner():
             P(*bad)
     # the largest accepted N still plans a positive split
     assert P(1, 32, 1, (1 << 30) - 1, 256) == 1
+
+
+def call_decode_noalloc(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=8, H_kv=2, Nq=1, Nk=1000, d=128, scale=0.1,
+                mask_kind=fa.FA_MASK_CAUSAL, window=0, dtype=fa.FA_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_decode_noalloc(*(args[n] for n in ("q", "k", "v", "o", "lse", "B", "H", "H_kv",
+                                                    "Nq", "Nk", "d", "scale", "mask_kind",
+                                                    "window", "dtype", "stream")))
+
+
+@pytest.mark.parametrize("kw", [dict(q=0), dict(Nq=0), dict(Nq=1001), dict(H_kv=3), dict(dtype=5),
+                                dict(mask_kind=fa.FA_MASK_SLIDING, window=0), dict(scale=-1.0),
+                                dict(o=O + 2), dict(o=K + 256)], ids=str)
+def test_decode_noalloc_checks_arguments_on_the_host(kw):
+    assert call_decode_noalloc(**kw) == fa.FA_ERR_INVALID_ARG, fa.fa_last_error()
+
+
+def test_decode_noalloc_rejects_sizes_beyond_its_scratch():
+    """The chunk partials of fa_decode_noalloc live in an 8 MiB device array:
+    larger needs are refused before any device call; sizes that fit get past
+    the check (no device here)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    big = dict(B=2, H=32, H_kv=1, Nk=1 << 20, q=1 << 40, o=(1 << 40) + (1 << 32),
+               k=(1 << 40) + (1 << 36), v=(1 << 40) + (2 << 36), lse=(1 << 40) + (3 << 36))
+    assert fa.fa_decode_workspace_bytes(2, 32, 1, 1, 1 << 20, 128) > 8 << 20
+    assert call_decode_noalloc(**big) == fa.FA_ERR_INVALID_ARG
+    assert "scratch" in fa.fa_last_error()
+    assert fa.fa_decode_workspace_bytes(8, 32, 8, 1, 32768, 128) <= 8 << 20
+    fits = dict(B=8, H=32, H_kv=8, Nk=32768, q=1 << 40, o=(1 << 40) + (1 << 32),
+                k=(1 << 40) + (1 << 36), v=(1 << 40) + (2 << 36), lse=(1 << 40) + (3 << 36))
+    assert call_decode_noalloc(**fits) == fa.FA_ERR_NO_DEVICE
