@@ -390,6 +390,79 @@ def attention_weights_rows(q_rows, pos, k, scale: float, mask: str = "none",
     return np.where(z > 0, w / np.where(z > 0, z, 1.0), 0.0)
 
 
+def attention_bwd_terms(q, k, v, do, o, lse, scale: float, mask: str = "none",
+                        window: int = 0, rows=None, keys=None) -> dict:
+    """Sums over the terms of the backward pass of one [N, d] slice, the sizes
+    against which its rounding is bounded (fp64, numpy).  o and lse are this
+    slice's forward result from ``attention`` (fp64).  With the definitions
+    of attn_bwd_oracle.c -- P_ij = exp(s_ij - lse_i) over visible pairs (0
+    elsewhere), s = scale q k^T, dP_ij = <do_i, v_j>, D_i = <do_i, o_i>,
+    dS_ij = P_ij (dP_ij - D_i) -- and Dm_i = sum_c |do_ic| max_j |v_jc| (an
+    upper bound of sum_c |do_ic| |o_ic|: o_i is a convex combination of the
+    v_j), for the query positions r in `rows` (default all) and the key
+    positions t in `keys` (default all), channel c:
+      dq[r, c] = scale sum_j dS_rj k_jc             the gradients themselves
+      dk[t, c] = scale sum_i dS_it q_ic             (evaluated from o, lse)
+      dv[t, c] = sum_i P_it do_ic
+      aq, ak, av: the same sums with every term replaced by its magnitude
+      rq[r, c] = scale sqrt(sum_j dS_rj^2 k_jc^2)    root-sum-squares of the
+      rk[t, c] = scale sqrt(sum_i dS_it^2 q_ic^2)    terms
+      rv[t, c] = sqrt(sum_i P_it^2 do_ic^2)
+      cq[r, c] = scale |sum_j P_rj k_jc|             coefficient of an error
+                                                     in D_r within dq[r, c]
+      ck[t, c] = scale sqrt(sum_i P_it^2 Dm_i^2 q_ic^2)
+      nq[r, c] = scale sqrt(sum_j vis_rj k_jc^2)     counts of the terms
+      nk[t, c] = scale sqrt(sum_i vis_it q_ic^2)     (for absolute errors per
+      nv[t, c] = sqrt(sum_i vis_it do_ic^2)          term)
+      dm[r] = Dm_r
+    |dq| <= aq, |dk| <= ak, |dv| <= av (triangle inequality)."""
+    q, k, v, do, o = _f64(q), _f64(k), _f64(v), _f64(do), _f64(o)
+    lse = _f64(lse)
+    N, d = q.shape
+    if k.shape != (N, d) or v.shape != (N, d) or do.shape != (N, d) or o.shape != (N, d) \
+            or lse.shape != (N,):
+        raise ValueError("q, k, v, do, o must be [N, d] and lse [N]")
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    keys = np.arange(N) if keys is None else np.asarray(keys, dtype=np.int64)
+    sc = float(scale)
+    D = (do * o).sum(axis=1)
+    Dm = np.abs(do) @ np.abs(v).max(axis=0)
+
+    def vis(ii, jj):
+        if mask == "none":
+            return np.ones((len(ii), len(jj)), dtype=bool)
+        i, j = ii[:, None], jj[None, :]
+        if mask == "causal":
+            return j <= i
+        return (j <= i) & (j > i - int(window))
+
+    out = {}
+    # query rows: full rows of P and dS
+    vr = vis(rows, np.arange(N))
+    P = np.where(vr, np.exp(np.where(vr, sc * (q[rows] @ k.T), 0.0) - lse[rows, None]), 0.0)
+    dS = P * (do[rows] @ v.T - D[rows, None])
+    out["dq"] = sc * (dS @ k)
+    out["aq"] = sc * (np.abs(dS) @ np.abs(k))
+    out["rq"] = sc * np.sqrt((dS * dS) @ (k * k))
+    out["cq"] = sc * np.abs(P @ k)
+    out["nq"] = sc * np.sqrt(vr.astype(np.float64) @ (k * k))
+    out["dm"] = Dm[rows]
+    # key columns: full columns of P and dS
+    vc = vis(np.arange(N), keys)
+    P = np.where(vc, np.exp(np.where(vc, sc * (q @ k[keys].T), 0.0) - lse[:, None]), 0.0)
+    dS = P * (do @ v[keys].T - D[:, None])
+    out["dk"] = sc * (dS.T @ q)
+    out["dv"] = P.T @ do
+    out["ak"] = sc * (np.abs(dS).T @ np.abs(q))
+    out["av"] = P.T @ np.abs(do)
+    out["rk"] = sc * np.sqrt((dS * dS).T @ (q * q))
+    out["rv"] = np.sqrt((P * P).T @ (do * do))
+    out["ck"] = sc * np.sqrt(((P * Dm[:, None]) ** 2).T @ (q * q))
+    out["nk"] = sc * np.sqrt(vc.astype(np.float64).T @ (q * q))
+    out["nv"] = np.sqrt(vc.astype(np.float64).T @ (do * do))
+    return out
+
+
 def visible(i: int, j: int, mask: str, window: int) -> bool:
     """The visibility predicate, one (query, key) pair at a time."""
     if mask == "none":

@@ -270,3 +270,103 @@ def test_shared_heads_equal_copied_heads_summed():
                                   "sliding", 5)[0] for h in range(H)]
     tq = torch_grads_gqa(q, k, v, do, 0.5, "sliding", 5)[0]
     assert not np.allclose(np.stack(wrong, axis=1), tq, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# attention_bwd_terms: the magnitude sums behind the backward's tolerance
+# ---------------------------------------------------------------------------
+def _terms_by_loops(q, k, v, do, scale, mask, window):
+    """The five sums of attention_bwd_terms from their definitions, one
+    (query, key, channel) at a time, with P from its own exponentials (no
+    oracle call): the brute-force pin."""
+    N, d = len(q), len(q[0])
+    vis = visible_matrix(N, mask, window)
+    P = [[0.0] * N for _ in range(N)]
+    for i in range(N):
+        s = [scale * sum(q[i][c] * k[j][c] for c in range(d)) for j in range(N)]
+        m = max(s[j] for j in range(N) if vis[i, j])
+        z = sum(math.exp(s[j] - m) for j in range(N) if vis[i, j])
+        for j in range(N):
+            P[i][j] = math.exp(s[j] - m) / z if vis[i, j] else 0.0
+    o = [[sum(P[i][j] * v[j][c] for j in range(N)) for c in range(d)] for i in range(N)]
+    D = [sum(do[i][c] * o[i][c] for c in range(d)) for i in range(N)]
+    vmax = [max(abs(v[j][c]) for j in range(N)) for c in range(d)]
+    Dm = [sum(abs(do[i][c]) * vmax[c] for c in range(d)) for i in range(N)]
+    dS = [[P[i][j] * (sum(do[i][c] * v[j][c] for c in range(d)) - D[i]) for j in range(N)]
+          for i in range(N)]
+    aq = [[scale * sum(abs(dS[i][j]) * abs(k[j][c]) for j in range(N)) for c in range(d)]
+          for i in range(N)]
+    ak = [[scale * sum(abs(dS[i][j]) * abs(q[i][c]) for i in range(N)) for c in range(d)]
+          for j in range(N)]
+    av = [[sum(P[i][j] * abs(do[i][c]) for i in range(N)) for c in range(d)] for j in range(N)]
+    rq = [[scale * math.sqrt(sum((dS[i][j] * k[j][c]) ** 2 for j in range(N))) for c in range(d)]
+          for i in range(N)]
+    rk = [[scale * math.sqrt(sum((dS[i][j] * q[i][c]) ** 2 for i in range(N))) for c in range(d)]
+          for j in range(N)]
+    rv = [[math.sqrt(sum((P[i][j] * do[i][c]) ** 2 for i in range(N))) for c in range(d)]
+          for j in range(N)]
+    cq = [[scale * abs(sum(P[i][j] * k[j][c] for j in range(N))) for c in range(d)]
+          for i in range(N)]
+    ck = [[scale * math.sqrt(sum((P[i][j] * Dm[i] * q[i][c]) ** 2 for i in range(N)))
+           for c in range(d)] for j in range(N)]
+    nq = [[scale * math.sqrt(sum(k[j][c] ** 2 for j in range(N) if vis[i, j])) for c in range(d)]
+          for i in range(N)]
+    nk = [[scale * math.sqrt(sum(q[i][c] ** 2 for i in range(N) if vis[i, j])) for c in range(d)]
+          for j in range(N)]
+    nv = [[math.sqrt(sum(do[i][c] ** 2 for i in range(N) if vis[i, j])) for c in range(d)]
+          for j in range(N)]
+    dq = [[scale * sum(dS[i][j] * k[j][c] for j in range(N)) for c in range(d)] for i in range(N)]
+    dk = [[scale * sum(dS[i][j] * q[i][c] for i in range(N)) for c in range(d)] for j in range(N)]
+    dv = [[sum(P[i][j] * do[i][c] for i in range(N)) for c in range(d)] for j in range(N)]
+    return {n: np.array(x) for n, x in (("aq", aq), ("ak", ak), ("av", av), ("rq", rq),
+                                          ("rk", rk), ("rv", rv), ("cq", cq), ("ck", ck),
+                                          ("nq", nq), ("nk", nk), ("nv", nv), ("dq", dq),
+                                          ("dk", dk), ("dv", dv), ("dm", Dm))}
+
+
+@pytest.mark.parametrize("mask,window", MASK_CASES)
+def test_bwd_terms_match_brute_force(mask, window):
+    N, d = 7, 3
+    q, k, v, do = (rand((N, d), 71 + s) for s in range(4))
+    scale = 0.8
+    o, lse = oracle.attention(q, k, v, scale, mask, window)
+    got = oracle.attention_bwd_terms(q, k, v, do, o, lse, scale, mask, window)
+    want = _terms_by_loops(q.tolist(), k.tolist(), v.tolist(), do.tolist(), scale, mask, window)
+    assert set(got) == set(want)
+    for n in want:
+        np.testing.assert_allclose(got[n], want[n], rtol=1e-12, atol=1e-14, err_msg=n)
+    # chosen rows and keys are the matching slices of the full result
+    rows, keys = np.array([6, 0, 3]), np.array([2, 5])
+    sub = oracle.attention_bwd_terms(q, k, v, do, o, lse, scale, mask, window, rows, keys)
+    for n in ("aq", "rq", "cq", "nq", "dq", "dm"):
+        np.testing.assert_allclose(sub[n], got[n][rows], rtol=1e-13, err_msg=n)
+    for n in ("ak", "av", "rk", "rv", "ck", "nk", "nv", "dk", "dv"):
+        np.testing.assert_allclose(sub[n], got[n][keys], rtol=1e-13, err_msg=n)
+
+
+@pytest.mark.parametrize("mask,window", MASK_CASES)
+def test_bwd_terms_bound_the_gradients(mask, window):
+    """aq, ak, av are the gradients' sums with every term made non-negative:
+    they bound |dq|, |dk|, |dv| (triangle inequality), and av equals dv when
+    every do entry is non-negative (all weights are)."""
+    N, d = 60, 8
+    q, k, v, do = (rand((N, d), 91 + s) for s in range(4))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = oracle.attention(q, k, v, scale, mask, window)
+    t = oracle.attention_bwd_terms(q, k, v, do, o, lse, scale, mask, window)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, scale, mask, window)
+    assert (np.abs(dq) <= t["aq"] * (1 + 1e-12) + 1e-15).all()
+    assert (np.abs(dk) <= t["ak"] * (1 + 1e-12) + 1e-15).all()
+    assert (np.abs(dv) <= t["av"] * (1 + 1e-12) + 1e-15).all()
+    # root-sum-squares never exceed the sums of magnitudes
+    assert (t["rq"] <= t["aq"] * (1 + 1e-12) + 1e-15).all()
+    assert (t["rk"] <= t["ak"] * (1 + 1e-12) + 1e-15).all()
+    assert (t["rv"] <= t["av"] * (1 + 1e-12) + 1e-15).all()
+    # its signed sums are the gradients of the C oracle
+    np.testing.assert_allclose(t["dq"], dq, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(t["dk"], dk, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(t["dv"], dv, rtol=1e-9, atol=1e-12)
+    dpos = np.abs(do)
+    t2 = oracle.attention_bwd_terms(q, k, v, dpos, o, lse, scale, mask, window)
+    _, _, dv2 = oracle.attention_bwd(q, k, v, dpos, scale, mask, window)
+    np.testing.assert_allclose(t2["av"], dv2, rtol=1e-12, atol=1e-15)
