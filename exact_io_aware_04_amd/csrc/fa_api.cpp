@@ -168,6 +168,17 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   p.n_row_tiles = (N + fa_rows_per_wg(in_dtype, d) - 1) / fa_rows_per_wg(in_dtype, d);
   p.xcd_split = (p.BH % 8 == 0) ? 1 : 0;
   p.heavy_first = mask_kind != FA_MASK_NONE ? 1 : 0;
+  // Persistent launch of the 16-bit kernel: one workgroup per compute unit
+  // (fewer when there are fewer tiles), a multiple of the 8 groups when
+  // every XCD owns its own heads.
+  {
+    const long long total = (long long)p.BH * p.n_row_tiles;
+    p.n_groups = p.xcd_split ? 8 : 1;
+    long long g = std::min<long long>(total, device_cus());
+    g = std::max<long long>(p.n_groups, g / p.n_groups * p.n_groups);
+    p.wg_per_group = (int)(g / p.n_groups);
+    p.tiles_per_group = (int)(total / p.n_groups);
+  }
   hipError_t e = in_dtype == FA_DTYPE_E4M3
                      ? fa_launch_fwd8(out_dtype, d, p, (hipStream_t)stream)
                      : fa_launch_fwd(in_dtype, out_dtype, d, p, (hipStream_t)stream);

@@ -76,6 +76,14 @@ __device__ __forceinline__ fa_u32x2 pack4(float a, float b, float c, float d) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A pointer that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ const unsigned char* uniform_ptr(const unsigned char* ptr) {
+  const unsigned long long v = (unsigned long long)ptr;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return (const unsigned char*)(((unsigned long long)hi << 32) | lo);
+}
+
 // Lanes l and l^32 hold the same query row: combine their values.  The swap
 // leaves each lane with its own value in one result and its partner's in the
 // other, so max / sum of the two results is the pair's max / sum.

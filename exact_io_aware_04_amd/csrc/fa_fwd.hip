@@ -54,9 +54,12 @@
 //    probabilities of exactly 0 where only some of its rows see them; fully
 //    visible ones run without a per-element mask, only boundary blocks
 //    evaluate the mask predicate.
-//  * Work order: longest row tiles first for masked inputs, and, when
-//    batch*heads is a multiple of 8, every XCD (blockIdx mod 8) processes its
-//    own set of heads so that a head's K/V stays within one L2.
+//  * Work order: one persistent workgroup per compute unit walks a list of
+//    row tiles, longest first for masked inputs (paired long with short),
+//    and, when batch*heads is a multiple of 8, every XCD (blockIdx mod 8)
+//    processes its own set of heads so that a head's K/V stays within one
+//    L2.  The K/V blocks of consecutive tiles stream through the same LDS
+//    rings, so the next tile's first blocks load during the current one.
 // fp32 inputs use v_mfma_f32_32x32x2f32 in a simpler kernel (4 wavefronts,
 // 128 query rows, register-staged and double-buffered K/V, 32-key blocks,
 // the reference raised only when a row maximum exceeds it by more than 8).
@@ -242,6 +245,12 @@ __device__ __forceinline__ void matrix_phase(fa_f32x16 (&acc)[D / 32], fa_f32x16
 // so the matrix cores and the vector ALUs work at the same time.  Wavefronts
 // 0-3 lead, 4-7 trail; a workgroup barrier between half steps keeps the two
 // groups in opposite phases.
+//
+// Persistent: one workgroup per compute unit walks its list of row tiles
+// (persist_tile).  The K/V blocks of consecutive tiles form one stream
+// through the LDS rings: the first two blocks of the next tile are loaded
+// during the last two steps of the current one, so a new tile starts with
+// its first blocks in LDS and no workgroup launch in between.
 template <int DT, int D, bool OUT_F32>
 __global__ void __launch_bounds__(FA_WAVES_16 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd16_kernel(FaFwdParams p) {
@@ -275,33 +284,7 @@ fa_fwd16_kernel(FaFwdParams p) {
   const int l32 = lane & 31;
   const int half = lane >> 5;
   const int N = p.N;
-
-  int bh, q0;
-  work_item<ROWS_WG>(p, bh, q0);
-  const int q1 = min(q0 + ROWS_WG, N);
-  // this wave's rows qb0 .. qb1-1; this lane's row qi
-  const int qb0 = q0 + wave * FA_ROW_BLOCK;
-  const int qb1 = min(qb0 + FA_ROW_BLOCK, N);
-  const int qi = qb0 + l32;
-
-  // query slice bh = b H + h reads key/value slice b H_kv + h / g = bh / g
   const size_t head_bytes = (size_t)N * ROWB;
-  const size_t kv_bytes = (size_t)(bh / p.kv_group) * head_bytes;
-  const unsigned char* Qh = (const unsigned char*)p.q + (size_t)bh * head_bytes;
-  const unsigned char* Kh = (const unsigned char*)p.k + kv_bytes;
-  const unsigned char* Vh = (const unsigned char*)p.v + kv_bytes;
-
-  int kv_lo, kv_hi;
-  fa_key_block_range(q0, q1, BC, N, p.mask_kind, p.window, &kv_lo, &kv_hi);
-
-  // Q fragment ks holds q[qi][16 ks + 8 half .. +7]; rows past N read row
-  // N-1 (no branch) and are never stored.
-  fa_u32x4 qf[NQF];
-  {
-    const unsigned char* qrow = Qh + (size_t)min(qi, N - 1) * ROWB;
-#pragma unroll
-    for (int ks = 0; ks < NQF; ++ks) qf[ks] = *(const fa_u32x4*)(qrow + ks * 32 + half * 16);
-  }
 
   // Global byte offset (within a block) of this lane's 16 bytes in a loading
   // wave's first one-kilobyte LDS piece, swizzle applied.  Piece i lies 4 KB
@@ -314,6 +297,7 @@ fa_fwd16_kernel(FaFwdParams p) {
     koff = r * ROWB + 16 * (pos ^ kswz<D>(r));
     voff = r * ROWB + 16 * (pos ^ vswz<D>(r));
   }
+  const unsigned my_off = lead ? koff : voff;
   // LDS read offsets: K slice s of row l32 (chunk 2s + half); V^T pieces for
   // output block cb (row 4half + t, columns 32cb + 16(lane/16 mod 2) + 4q).
   unsigned kread[NQF], vread[NCB];
@@ -326,14 +310,17 @@ fa_fwd16_kernel(FaFwdParams p) {
       vread[cb] = (4 * half + t) * ROWB + 64 * (cb ^ (D == 128 ? t : (t >> 1))) + 32 * (g & 1) + 8 * q;
   }
 
-  // K or V block kt -> LDS slot.  The descriptor's base is the block's first
-  // key and its size stops at key N, so rows past N read as zeros.  (The
-  // offsets are passed as int prvalues: handing the builtin the captured
-  // array element itself keeps hipcc's host pass from emitting the kernel's
-  // launch stub.)
+  // K or V block kt of a head -> LDS slot.  The descriptor's base is the
+  // block's first key and its size stops at key N, so rows past N read as
+  // zeros (a block wholly past N, the padding of a one-block tile, reads
+  // zeros only).  (The offsets are passed as int prvalues: handing the
+  // builtin the captured array element itself keeps hipcc's host pass from
+  // emitting the kernel's launch stub.)
   auto issue = [&](const unsigned char* base, unsigned off, FA_AS3 unsigned char* dst, int kt) {
     const int k0 = kt * BC;
-    const int nb = (min(N - k0, BC)) * ROWB;
+    // (readfirstlane: the clamp would otherwise become a vector instruction
+    // and the descriptor a per-lane value)
+    const int nb = __builtin_amdgcn_readfirstlane(max(min(N - k0, BC), 0) * ROWB);
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * ROWB), 0, nb, FA_BUF_WORD3);
 #pragma unroll
@@ -342,25 +329,56 @@ fa_fwd16_kernel(FaFwdParams p) {
           rsrc, (FA_AS3 void*)(dst + (i * NL + wave % NL) * 1024), 16, (int)off, i * NL * 1024, 0, 0);
   };
 
-  fa_f32x16 acc[NCB];  // O^T: acc[cb] holds columns 32cb.., row qi
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-  // reference (base 2) and this lane's sum of unrounded probabilities; the
-  // row sums of the rounded ones accumulate on the matrix core, in lsum
-  float m_ref = FA_NEG_INF, l_lane = 0.f;
-  fa_f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
   const fa_u32x4 sel = rowsum_selector<DT>(lane);
   const float c2 = p.scale_log2;
+  const float inv_c2 = 1.f / p.scale_log2;
   const int n_row_blocks = (N + FA_ROW_BLOCK - 1) / FA_ROW_BLOCK;
   const int n_key_blocks = (N + BC - 1) / BC;
 
-  // Carried between the phases: scores of the current block (matrix phase
-  // -> softmax phase) and its rounded probabilities (softmax phase -> the
-  // next matrix phase).  s[kb][r] is key k0 + 32kb + 8(r/4) + 4half + r%4 of
-  // row qi; P^T operand (kb, t) holds registers 8t..8t+7 of s[kb], i.e. keys
-  // 32kb + 16t + {4half + 0..3, 8 + 4half + 0..3}.
+  // Tile state.  A tile is (bh, q0): batch*head bh, query rows q0 ..
+  // q0+ROWS_WG-1.  Its key blocks kv_lo .. kv_end-1 are those some of its
+  // rows see; the tile runs at least two (kv_hi = max(kv_end, kv_lo + 2):
+  // the padding block, if any, lies past N and is skipped by every wave),
+  // so that the next tile's first two blocks can always be loaded during the
+  // last two steps of this one.  Query slice bh = b H + h reads key/value
+  // slice b H_kv + h / g = bh / g.
+  struct Tile {
+    int bh, q0, kv_lo, kv_end, kv_hi;
+    const unsigned char *Kh, *Vh;
+  };
+  auto make_tile = [&](int bh_, int q0_) {
+    Tile t;
+    t.bh = bh_;
+    t.q0 = q0_;
+    fa_key_block_range(q0_, min(q0_ + ROWS_WG, N), BC, N, p.mask_kind, p.window, &t.kv_lo,
+                       &t.kv_end);
+    t.kv_hi = max(t.kv_end, t.kv_lo + 2);
+    const size_t kv_bytes = (size_t)(bh_ / p.kv_group) * head_bytes;
+    t.Kh = (const unsigned char*)p.k + kv_bytes;
+    t.Vh = (const unsigned char*)p.v + kv_bytes;
+    return t;
+  };
+
+  int tile_k = 0, nbh = 0, nq0 = 0;
+  {
+    int bh0, q00;
+    if (!persist_tile(p, 0, bh0, q00, ROWS_WG)) return;  // no work for this workgroup
+    nbh = bh0;
+    nq0 = q00;
+  }
+  Tile cur = make_tile(nbh, nq0);
+  bool has_next = persist_tile(p, 1, nbh, nq0, ROWS_WG);
+  Tile nxt = make_tile(has_next ? nbh : cur.bh, has_next ? nq0 : cur.q0);
+
+  // Carried between tiles and steps: the output accumulators, the row's
+  // reference (base 2) and sums, the scores of the current block (matrix
+  // phase -> softmax phase) and its rounded probabilities (softmax phase ->
+  // the next matrix phase).  s[kb][r] is key k0 + 32kb + 8(r/4) + 4half +
+  // r%4 of row qi; P^T operand (kb, t) holds registers 8t..8t+7 of s[kb],
+  // i.e. keys 32kb + 16t + {4half + 0..3, 8 + 4half + 0..3}.
+  fa_f32x16 acc[NCB];  // O^T: acc[cb] holds columns 32cb.., row qi
+  float m_ref, l_lane;
+  fa_f32x4 lsum;
   fa_f32x16 sc[NKB];
   fa_u32x4 pf[NKB][2];
   // Start value of the score accumulators: -m_use / c2 in all 16 registers
@@ -372,177 +390,267 @@ fa_fwd16_kernel(FaFwdParams p) {
   // more VGPR operands costs one extra issue cycle of four).
   fa_f32x16 sc0;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sc0[r] = 0.f;
-  const float inv_c2 = 1.f / p.scale_log2;
-#pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int t = 0; t < 2; ++t) pf[kb][t] = fa_u32x4{0u, 0u, 0u, 0u};
 
-  // Matrix phase of step kt: O^T += V^T P^T for block kt-1 (V slot vs) and
-  // S^T = K Q^T for block kt (K slot ks).  It runs in full even where the
-  // row block sees no key of one of the blocks (the workgroup's barriers
-  // pace every wave anyway, and one code path keeps the registers in
-  // place): the probabilities of a skipped block are 0, which adds exactly
-  // 0 to O, and the scores of a skipped block are never used.
-  auto phase_mfma = [&](int ks, int vs) {
-    matrix_phase<DT, D>(acc, sc, lsum, sel, sc0, pf, qf, kbuf(ks), vbuf(vs), kread, vread);
-  };
-  // Softmax phase of block kt (classification cls).  Fast path (fully
-  // visible block, row already started): p = 2^t straight from the scores;
-  // a lane's sum of its 32 probabilities at most 2^8 bounds each of them by
-  // 2^8 (no score more than 8 base-2 units above the reference).  Exact path
-  // (boundary block, a row's first block, or a lane's sum above 2^8,
-  // infinite or NaN): mask, row maximum, new reference at the exact maximum,
-  // rescale of O and the sums, probabilities again.
-  auto phase_softmax = [&](int kt, int cls) {
-    if (cls == FA_TILE_SKIP) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) pf[kb][t] = fa_u32x4{0u, 0u, 0u, 0u};
-      return;
-    }
-    float pr[NKB][16];
-    float psum = 0.f;
-    bool exact = cls == FA_TILE_PARTIAL || __ballot(m_ref == FA_NEG_INF);
-    if (!exact) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pr[kb][r] = exp2_hw(sc[kb][r] * c2);
-          psum += pr[kb][r];
-        }
-      exact = __ballot(!(psum <= 256.f));
-    }
-    if (exact) {
-      if (cls == FA_TILE_PARTIAL) apply_mask<NKB>(sc, kt * BC, qi, half, N, p.mask_kind, p.window);
-      const float m_use = m_ref == FA_NEG_INF ? 0.f : m_ref;
-      float mx = FA_NEG_INF;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      mx = pair_max(mx) * c2;  // block maximum of t (-inf: nothing visible)
-      const float m_new = fmaxf(m_ref, mx == FA_NEG_INF ? FA_NEG_INF : m_use + mx);
-      const float alpha = m_new > m_ref ? (m_ref == FA_NEG_INF ? 0.f : exp2_hw(m_ref - m_new)) : 1.f;
-      m_ref = m_new;
-      l_lane *= alpha;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lsum[r] *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
-      const float shift = m_ref == FA_NEG_INF ? 0.f : m_use - m_ref;
-      psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pr[kb][r] = exp2_hw(__builtin_fmaf(sc[kb][r], c2, shift));
-          psum += pr[kb][r];
-        }
-      const float mn = m_ref == FA_NEG_INF ? 0.f : -m_ref * inv_c2;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc0[r] = mn;
-    }
-    // Two row sums.  The output is normalised by the sum of the ROUNDED
-    // probabilities (the values the matrix core multiplies V with; summed on
-    // the matrix core in the next matrix phase), so output and normaliser
-    // use identical weights: constant V comes out exact and a dominant key
-    // is selected exactly.  lse uses the sum of the unrounded probabilities,
-    // which rounding to 16 bits would otherwise move by up to 2^-9.
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) pf[kb][t] = pack8<DT>(&pr[kb][8 * t]);
-    l_lane += psum;
-  };
-
-  // Loads.  K(j) and V(j) live in ring slot (j - kv_lo) mod 3.  At the end
-  // of its softmax phase kt (where it would otherwise wait at the barrier) a
-  // leading wave issues its share of K(kt+2), a trailing wave its share of
-  // V(kt+2), into the slots of block kt-1, whose last reader (matrix phase
-  // kt-1 for K, matrix phase kt for V) has passed a barrier since.  The wait
-  // that follows lets these stay in flight, so the wave's loads of the
-  // previous step, K(kt+1) or V(kt+1), have landed (loads complete in issue
-  // order).
-  auto issue_step = [&](int kt, int s) {
-    if (kt + 2 < kv_hi) {
-      if (lead)
-        issue(Kh, koff, kbuf((s + 2) % 3), kt + 2);
-      else
-        issue(Vh, voff, vbuf((s + 2) % 3), kt + 2);
-    }
-  };
-  auto wait_step = [&](int kt) {
-    if (kt + 2 < kv_hi)
-      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(LPW));
-    else
-      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
-  };
-
-  // Every wave runs, for kt = kv_lo .. kv_hi: matrix phase kt (scores of
-  // block kt, P V of block kt-1), barrier, softmax phase kt, barrier.  The
-  // trailing waves pass one barrier before their first step, the leading
-  // ones one after their last, so a trailing wave's matrix phase kt runs
-  // beside the leading waves' softmax phase kt, and its softmax phase kt
-  // beside their matrix phase kt+1.  In half steps h (the intervals between
-  // consecutive barriers; h = 2(kt - kv_lo) is the leading waves' matrix
-  // phase kt): matrix phase kt reads K(kt) and V(kt-1) in h and h + 1;
-  // K(kt+2) is issued at the end of h + 1 and V(kt+2) at the end of h + 2,
-  // after every wave has finished its LDS reads of the slots they replace
-  // (lgkmcnt(0) before each barrier); K(kt+1) and V(kt+1), issued in the
-  // previous step, are waited for before the barriers that end h + 1 and
-  // h + 2, ahead of matrix phases kt+1 and kt+2 that read them.
-  auto step = [&](int kt, int s) {
-    int cls_cur = FA_TILE_SKIP;
-    if (kt < kv_hi) {
-      cls_cur = fa_classify(qb0, qb1, kt * BC, BC, N, p.mask_kind, p.window);
-      if (p.tiles && lane == 0 && qb0 < N)
-        p.tiles[((size_t)bh * n_row_blocks + qb0 / FA_ROW_BLOCK) * n_key_blocks + kt] =
-            (unsigned char)(cls_cur + 1);
-    }
-    phase_mfma(s, (s + 2) % 3);
-    __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
-    barrier_nofence();
-    phase_softmax(kt, cls_cur);
-    issue_step(kt, s);
-    wait_step(kt);
-    __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
-    barrier_nofence();
-  };
-
-  // Every workgroup has at least one key block: row q0 < N always sees key
-  // q0 itself (the diagonal is visible under every mask).  Prologue: K and V
-  // of the first two blocks, and zeros in the V slot that the first step's
-  // (probability 0) P V product reads.
-  if (lead) {
-    issue(Kh, koff, kbuf(0), kv_lo);
-    if (kv_lo + 1 < kv_hi) issue(Kh, koff, kbuf(1), kv_lo + 1);
-  } else {
-    issue(Vh, voff, vbuf(0), kv_lo);
-    if (kv_lo + 1 < kv_hi) issue(Vh, voff, vbuf(1), kv_lo + 1);
-  }
+  // Prologue of the first tile: its first two K and V blocks into ring slots
+  // 0 and 1, and zeros in V slot 2, which the first step's (probability 0)
+  // P V product reads.  Later tiles find their first two blocks already
+  // loaded, and their first P V product reads the previous tile's last V
+  // block (finite values, times probability 0).
+  issue(lead ? cur.Kh : cur.Vh, my_off, lead ? kbuf(0) : vbuf(0), cur.kv_lo);
+  issue(lead ? cur.Kh : cur.Vh, my_off, lead ? kbuf(1) : vbuf(1), cur.kv_lo + 1);
 #pragma unroll
   for (int i = 0; i < TILEB / (NW * 64 * 16); ++i)
     *(FA_AS3 fa_u32x4*)(vbuf(2) + (i * NW * 64 + tid) * 16) = fa_u32x4{0u, 0u, 0u, 0u};
   static_assert(TILEB % (NW * 64 * 16) == 0, "zero fill must cover the slot");
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (!lead) barrier_nofence();
-  for (int kt = kv_lo;;) {
-    step(kt, 0);
-    if (++kt > kv_hi) break;
-    step(kt, 1);
-    if (++kt > kv_hi) break;
-    step(kt, 2);
-    if (++kt > kv_hi) break;
+
+  // Q fragment ks holds q[qi][16 ks + 8 half .. +7] of the current tile;
+  // rows past N read row N-1 (no branch) and are never stored.  The next
+  // tile's fragments are loaded before the current tile's output is stored,
+  // so that waiting for them does not wait for the stores.
+  fa_u32x4 qf[NQF];
+  auto load_q = [&](int bh_, int q0_) {
+    const int row = min(q0_ + wave * FA_ROW_BLOCK + l32, N - 1);
+    const unsigned char* qrow = (const unsigned char*)p.q + (size_t)bh_ * head_bytes + (size_t)row * ROWB;
+#pragma unroll
+    for (int ks = 0; ks < NQF; ++ks) qf[ks] = *(const fa_u32x4*)(qrow + ks * 32 + half * 16);
+  };
+  load_q(cur.bh, cur.q0);
+
+  int ph = 0;  // ring slot of the current tile's first block
+  for (;;) {
+    const int bh = cur.bh, q0 = cur.q0;
+    const int kv_lo = cur.kv_lo, kv_hi = cur.kv_hi, kv_end = cur.kv_end;
+    const int q1 = min(q0 + ROWS_WG, N);
+    // this wave's rows qb0 .. qb1-1; this lane's row qi
+    const int qb0 = q0 + wave * FA_ROW_BLOCK;
+    const int qb1 = min(qb0 + FA_ROW_BLOCK, N);
+    const int qi = qb0 + l32;
+    (void)q1;
+    // Fully visible key blocks of this wave's rows form one range
+    // [full_lo, full_hi) (the classes along the keys run SKIP, PARTIAL,
+    // FULL, PARTIAL, SKIP); blocks inside it need no classification in the
+    // loop.  Both ends are found within eight blocks of the tile's ends,
+    // else the range is left empty (every block classified).
+    int full_lo = kv_lo, full_hi = kv_end;
+    for (int it = 0; it < 8 && full_lo < kv_end &&
+                     fa_classify(qb0, qb1, full_lo * BC, BC, N, p.mask_kind, p.window) != FA_TILE_FULL;
+         ++it)
+      ++full_lo;
+    for (int it = 0; it < 8 && full_hi > full_lo &&
+                     fa_classify(qb0, qb1, (full_hi - 1) * BC, BC, N, p.mask_kind, p.window) != FA_TILE_FULL;
+         ++it)
+      --full_hi;
+    if (full_lo >= full_hi ||
+        fa_classify(qb0, qb1, full_lo * BC, BC, N, p.mask_kind, p.window) != FA_TILE_FULL ||
+        fa_classify(qb0, qb1, (full_hi - 1) * BC, BC, N, p.mask_kind, p.window) != FA_TILE_FULL) {
+      full_lo = kv_lo;
+      full_hi = kv_lo;
+    }
+
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+    // reference (base 2) and this lane's sum of unrounded probabilities; the
+    // row sums of the rounded ones accumulate on the matrix core, in lsum
+    m_ref = FA_NEG_INF;
+    l_lane = 0.f;
+    lsum = fa_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc0[r] = 0.f;
+
+    // Tile-decision record (fa_fwd_record_tiles): the class of key block kt
+    // for this wave's row block, plus one.
+    auto record = [&](int kt, int cls) {
+      if (lane == 0 && qb0 < N)
+        p.tiles[((size_t)bh * n_row_blocks + qb0 / FA_ROW_BLOCK) * n_key_blocks + kt] =
+            (unsigned char)(cls + 1);
+    };
+    // Matrix phase of step kt: O^T += V^T P^T for block kt-1 (V slot vs) and
+    // S^T = K Q^T for block kt (K slot ks).  It runs in full even where the
+    // row block sees no key of one of the blocks (the workgroup's barriers
+    // pace every wave anyway, and one code path keeps the registers in
+    // place): the probabilities of a skipped block are 0, which adds exactly
+    // 0 to O, and the scores of a skipped block are never used.
+    auto phase_mfma = [&](int ks, int vs) {
+      matrix_phase<DT, D>(acc, sc, lsum, sel, sc0, pf, qf, kbuf(ks), vbuf(vs), kread, vread);
+    };
+    // Softmax phase of block kt (classification cls).  Fast path (fully
+    // visible block, row already started): p = 2^t straight from the scores;
+    // a lane's sum of its 32 probabilities at most 2^8 bounds each of them
+    // by 2^8 (no score more than 8 base-2 units above the reference).  Exact
+    // path (boundary block, a row's first block, or a lane's sum above 2^8,
+    // infinite or NaN): mask, row maximum, new reference at the exact
+    // maximum, rescale of O and the sums, probabilities again.
+    auto phase_softmax = [&](int kt, int cls) {
+      if (cls == FA_TILE_SKIP) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) pf[kb][t] = fa_u32x4{0u, 0u, 0u, 0u};
+        return;
+      }
+      float pr[NKB][16];
+      float psum = 0.f;
+      bool exact = cls == FA_TILE_PARTIAL || __ballot(m_ref == FA_NEG_INF);
+      if (!exact) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            pr[kb][r] = exp2_hw(sc[kb][r] * c2);
+            psum += pr[kb][r];
+          }
+        exact = __ballot(!(psum <= 256.f));
+      }
+      if (exact) {
+        if (cls == FA_TILE_PARTIAL) apply_mask<NKB>(sc, kt * BC, qi, half, N, p.mask_kind, p.window);
+        const float m_use = m_ref == FA_NEG_INF ? 0.f : m_ref;
+        float mx = FA_NEG_INF;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+        mx = pair_max(mx) * c2;  // block maximum of t (-inf: nothing visible)
+        const float m_new = fmaxf(m_ref, mx == FA_NEG_INF ? FA_NEG_INF : m_use + mx);
+        const float alpha = m_new > m_ref ? (m_ref == FA_NEG_INF ? 0.f : exp2_hw(m_ref - m_new)) : 1.f;
+        m_ref = m_new;
+        l_lane *= alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lsum[r] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+        const float shift = m_ref == FA_NEG_INF ? 0.f : m_use - m_ref;
+        psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            pr[kb][r] = exp2_hw(__builtin_fmaf(sc[kb][r], c2, shift));
+            psum += pr[kb][r];
+          }
+        const float mn = m_ref == FA_NEG_INF ? 0.f : -m_ref * inv_c2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc0[r] = mn;
+      }
+      // Two row sums.  The output is normalised by the sum of the ROUNDED
+      // probabilities (the values the matrix core multiplies V with; summed
+      // on the matrix core in the next matrix phase), so output and
+      // normaliser use identical weights: constant V comes out exact and a
+      // dominant key is selected exactly.  lse uses the sum of the unrounded
+      // probabilities, which rounding to 16 bits would otherwise move by up
+      // to 2^-9.
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) pf[kb][t] = pack8<DT>(&pr[kb][8 * t]);
+      l_lane += psum;
+    };
+
+    // Loads.  The blocks of this tile and the next form one stream through
+    // the rings: block kt of this tile lives in slot (ph + kt - kv_lo) mod
+    // 3, the next tile's first block in slot (ph + kv_hi - kv_lo) mod 3.  At
+    // the end of its softmax phase kt (where it would otherwise wait at the
+    // barrier) a leading wave issues its share of the K block two places
+    // further in the stream, a trailing wave its share of that V block, into
+    // the slots of block kt-1, whose last reader (matrix phase kt-1 for K,
+    // matrix phase kt for V) has passed a barrier since: block kt+2 of this
+    // tile, or for kt = kv_hi-2 and kv_hi-1 the next tile's first two
+    // blocks; the last step (kt = kv_hi, P V only) issues nothing.  The wait
+    // that follows lets these stay in flight, so the wave's loads of the
+    // previous step have landed (loads complete in issue order).
+    // (each wave loads one matrix: the leading ones K, the trailing ones V;
+    // the values are the same in every lane, which readfirstlane makes
+    // visible to the compiler, keeping the buffer descriptors in SGPRs)
+    const unsigned char* my_cur = uniform_ptr(lead ? cur.Kh : cur.Vh);
+    const unsigned char* my_nxt = uniform_ptr(lead ? nxt.Kh : nxt.Vh);
+    const int nxt_lo = __builtin_amdgcn_readfirstlane(nxt.kv_lo);
+    auto issued = [&](int kt) { return kt + 2 < kv_hi || (kt < kv_hi && has_next); };
+    auto issue_step = [&](int kt, int s) {
+      if (issued(kt)) {
+        const bool here = kt + 2 < kv_hi;
+        issue(here ? my_cur : my_nxt, my_off, lead ? kbuf((s + 2) % 3) : vbuf((s + 2) % 3),
+              here ? kt + 2 : nxt_lo + (kt + 2 - kv_hi));
+      }
+    };
+    auto wait_step = [&](int kt) {
+      if (issued(kt))
+        __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(LPW));
+      else
+        __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
+    };
+
+    // Every wave runs, for kt = kv_lo .. kv_hi: matrix phase kt (scores of
+    // block kt, P V of block kt-1), barrier, softmax phase kt, barrier.  The
+    // trailing waves pass one barrier before their first step, the leading
+    // ones one after their last, so a trailing wave's matrix phase kt runs
+    // beside the leading waves' softmax phase kt, and its softmax phase kt
+    // beside their matrix phase kt+1.  In half steps h (the intervals
+    // between consecutive barriers; h = 2(kt - kv_lo) is the leading waves'
+    // matrix phase kt): matrix phase kt reads K(kt) and V(kt-1) in h and
+    // h + 1; K(kt+2) is issued at the end of h + 1 and V(kt+2) at the end of
+    // h + 2, after every wave has finished its LDS reads of the slots they
+    // replace (lgkmcnt(0) before each barrier); K(kt+1) and V(kt+1), issued
+    // in the previous step, are waited for before the barriers that end
+    // h + 1 and h + 2, ahead of matrix phases kt+1 and kt+2 that read them.
+    // Tiles follow each other with the same barrier count in both groups.
+    auto step = [&](int kt, int s) {
+      int cls_cur = FA_TILE_FULL;
+      if (kt < full_lo || kt >= full_hi) {
+        cls_cur = kt < kv_end ? fa_classify(qb0, qb1, kt * BC, BC, N, p.mask_kind, p.window)
+                              : FA_TILE_SKIP;
+        if (p.tiles && kt < kv_end) record(kt, cls_cur);
+      }
+      phase_mfma(s, (s + 2) % 3);
+      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
+      barrier_nofence();
+      phase_softmax(kt, cls_cur);
+      issue_step(kt, s);
+      wait_step(kt);
+      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
+      barrier_nofence();
+    };
+
+    if (p.tiles)
+      for (int kt = full_lo; kt < full_hi; ++kt) record(kt, FA_TILE_FULL);
+    if (!lead) barrier_nofence();
+    // steps kt = kv_lo .. kv_hi; step kt uses ring slot (ph + kt - kv_lo)
+    // mod 3 (entered at the slot of the tile's first block)
+    {
+      int kt = kv_lo;
+      int entry = ph;
+      for (;;) {
+        if (entry == 0) {
+          step(kt, 0);
+          if (++kt > kv_hi) break;
+        }
+        if (entry <= 1) {
+          step(kt, 1);
+          if (++kt > kv_hi) break;
+        }
+        step(kt, 2);
+        if (++kt > kv_hi) break;
+        entry = 0;
+      }
+    }
+    if (lead) barrier_nofence();
+    if (has_next) load_q(nxt.bh, nxt.q0);
+    store_output<DT, D, OUT_F32>(p, acc, m_ref, pair_sum(l_lane), lsum[0], bh, qi, half);
+
+    if (!has_next) break;
+    ph = (ph + (kv_hi - kv_lo)) % 3;
+    cur = nxt;
+    ++tile_k;
+    has_next = persist_tile(p, tile_k + 1, nbh, nq0, ROWS_WG);
+    if (has_next) nxt = make_tile(nbh, nq0);
   }
-  if (lead) barrier_nofence();
-  store_output<DT, D, OUT_F32>(p, acc, m_ref, pair_sum(l_lane), lsum[0], bh, qi, half);
 }
 
 // ---------------------------------------------------------------------------
@@ -1015,7 +1123,9 @@ hipError_t launch(const FaFwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((fa_fwd16_wide_kernel<DT, OUT_F32>), grid, dim3(FA_WAVES_WIDE * 64), 0,
                        stream, p);
   else
-    hipLaunchKernelGGL((fa_fwd16_kernel<DT, D, OUT_F32>), grid, dim3(FA_WAVES_16 * 64), 0, stream, p);
+    hipLaunchKernelGGL((fa_fwd16_kernel<DT, D, OUT_F32>),
+                       dim3((unsigned)(p.n_groups * p.wg_per_group)), dim3(FA_WAVES_16 * 64), 0,
+                       stream, p);
   return hipGetLastError();
 }
 

@@ -23,6 +23,13 @@ struct FaFwdParams {
   int n_row_tiles;        // ceil(N / rows_per_workgroup)
   int xcd_split;          // 1: give each XCD its own heads (BH % 8 == 0)
   int heavy_first;        // 1: longest row tiles launched first (masks)
+  // Persistent launches (the 16-bit kernel at d <= 128): n_groups groups of
+  // wg_per_group workgroups (grid n_groups * wg_per_group); group x = blockIdx
+  // mod n_groups takes tiles_per_group tiles (8 groups: the XCDs, each with
+  // its own BH / 8 heads; 1 group: all tiles).
+  int n_groups;
+  int wg_per_group;
+  int tiles_per_group;
 };
 
 // Backward pass (fa_bwd.hip).
