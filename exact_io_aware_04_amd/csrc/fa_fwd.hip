@@ -139,6 +139,54 @@ __device__ __forceinline__ void store_output(const FaFwdParams& p, const fa_f32x
   if (half == 0) p.lse[row] = lse;
 }
 
+// 16-bit output of one wave's 32 rows through 16 rows of LDS scratch
+// (`stage`, 32 D bytes private to the wave), in two rounds of 16 rows.  Straight from
+// the accumulators each store instruction would cover 32 rows with 16 bytes
+// each; restaged, each covers 4 (d = 128) or 8 (d = 64) whole rows.  Round
+// j: the lanes of rows 16j .. 16j+15 write their 4-column pieces (row r at
+// r * 2D bytes, 16-byte chunk c at position c ^ (r mod chunks per row), so
+// that the 32 writing lanes of one instruction hit distinct banks), then
+// every lane reads one 16-byte chunk and stores it (rows past N skipped).
+// lse as in store_output.
+template <int DT, int D>
+__device__ __forceinline__ void store_output_staged(const FaFwdParams& p, const fa_f32x16 (&acc)[D / 32],
+                                                    float m_ref, float l_tot, float lq_tot, int bh,
+                                                    int qb0, int lane, FA_AS3 unsigned char* stage) {
+  constexpr int ROWB = 2 * D, CPR = ROWB / 16;  // bytes and 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                  // rows per read instruction
+  const int N = p.N;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int qi = qb0 + l32;
+  const float inv = lq_tot > 0.f ? 1.f / lq_tot : 0.f;
+  const float lse = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * FA_LN2 : FA_NEG_INF;
+  unsigned char* O = (unsigned char*)p.o + ((size_t)bh * N) * ROWB;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if ((l32 >> 4) == j) {
+      const int r = l32 & 15;
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ch = (4 * cb + g) ^ (r & (CPR - 1));
+          *(FA_AS3 fa_u32x2*)(stage + r * ROWB + 16 * ch + 8 * half) =
+              pack4<DT>(acc[cb][4 * g] * inv, acc[cb][4 * g + 1] * inv, acc[cb][4 * g + 2] * inv,
+                        acc[cb][4 * g + 3] * inv);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
+#pragma unroll
+    for (int i = 0; i < 16 / RPI; ++i) {
+      const int r = i * RPI + lane / CPR, pos = lane % CPR;
+      const fa_u32x4 val = *(const FA_AS3 fa_u32x4*)(stage + r * ROWB + 16 * pos);
+      const int row = qb0 + 16 * j + r;
+      if (row < N) *(fa_u32x4*)(O + (size_t)row * ROWB + 16 * (pos ^ (r & (CPR - 1)))) = val;
+    }
+    __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
+  }
+  if (half == 0 && qi < N) p.lse[(size_t)bh * N + qi] = lse;
+}
+
 // ---------------------------------------------------------------------------
 // bf16 / f16 kernel
 // ---------------------------------------------------------------------------
@@ -642,7 +690,20 @@ fa_fwd16_kernel(FaFwdParams p) {
     }
     if (lead) barrier_nofence();
     if (has_next) load_q(nxt.bh, nxt.q0);
-    store_output<DT, D, OUT_F32>(p, acc, m_ref, pair_sum(l_lane), lsum[0], bh, qi, half);
+    if constexpr (OUT_F32) {
+      store_output<DT, D, OUT_F32>(p, acc, m_ref, pair_sum(l_lane), lsum[0], bh, qi, half);
+    } else {
+      // Scratch for the restaged output: ring slot (ph + kv_hi - kv_lo + 2)
+      // mod 3, which holds this tile's last block -- K no longer read, V
+      // read next only by the next tile's first step, with probability 0
+      // (any finite values do) -- and is refilled only at the end of that
+      // step's softmax phase.  Waves 0-3 use the K slot, 4-7 the V slot,
+      // 16 rows each (4 KB at d = 128, 2 KB at d = 64: a slot holds 64 rows).
+      static_assert(NL * 16 * ROWB <= TILEB, "four 16-row stages must fit in one slot");
+      const int sl = (ph + (kv_hi - kv_lo) + 2) % 3;
+      FA_AS3 unsigned char* stage = (lead ? kbuf(sl) : vbuf(sl)) + (wave % NL) * (16 * ROWB);
+      store_output_staged<DT, D>(p, acc, m_ref, pair_sum(l_lane), lsum[0], bh, qb0, lane, stage);
+    }
 
     if (!has_next) break;
     ph = (ph + (kv_hi - kv_lo)) % 3;
