@@ -175,14 +175,17 @@ __device__ __forceinline__ void store_output_staged(const FaFwdParams& p, const 
         }
     }
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
+    fa_u32x4 val[16 / RPI];  // all reads first, one wait, then the stores
+#pragma unroll
+    for (int i = 0; i < 16 / RPI; ++i)
+      val[i] = *(const FA_AS3 fa_u32x4*)(stage + (i * RPI + lane / CPR) * ROWB + 16 * (lane % CPR));
+    __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
 #pragma unroll
     for (int i = 0; i < 16 / RPI; ++i) {
       const int r = i * RPI + lane / CPR, pos = lane % CPR;
-      const fa_u32x4 val = *(const FA_AS3 fa_u32x4*)(stage + r * ROWB + 16 * pos);
       const int row = qb0 + 16 * j + r;
-      if (row < N) *(fa_u32x4*)(O + (size_t)row * ROWB + 16 * (pos ^ (r & (CPR - 1)))) = val;
+      if (row < N) *(fa_u32x4*)(O + (size_t)row * ROWB + 16 * (pos ^ (r & (CPR - 1)))) = val[i];
     }
-    __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
   }
   if (half == 0 && qi < N) p.lse[(size_t)bh * N + qi] = lse;
 }
@@ -457,9 +460,7 @@ fa_fwd16_kernel(FaFwdParams p) {
   __syncthreads();
 
   // Q fragment ks holds q[qi][16 ks + 8 half .. +7] of the current tile;
-  // rows past N read row N-1 (no branch) and are never stored.  The next
-  // tile's fragments are loaded before the current tile's output is stored,
-  // so that waiting for them does not wait for the stores.
+  // rows past N read row N-1 (no branch) and are never stored.
   fa_u32x4 qf[NQF];
   auto load_q = [&](int bh_, int q0_) {
     const int row = min(q0_ + wave * FA_ROW_BLOCK + l32, N - 1);
@@ -688,8 +689,12 @@ fa_fwd16_kernel(FaFwdParams p) {
         entry = 0;
       }
     }
-    if (lead) barrier_nofence();
+    // The next tile's Q rows: loaded before the leading waves' last barrier
+    // (where they wait for the trailing waves' last softmax phase), and
+    // before this tile's output is stored.  (A load inside the step loop
+    // would make the compiler wait for it before every score product.)
     if (has_next) load_q(nxt.bh, nxt.q0);
+    if (lead) barrier_nofence();
     if constexpr (OUT_F32) {
       store_output<DT, D, OUT_F32>(p, acc, m_ref, pair_sum(l_lane), lsum[0], bh, qi, half);
     } else {
