@@ -313,13 +313,49 @@ def record_traffic(fetch_csv: str, write_csv: str, workload: str, command: str):
     print(json.dumps(rec["workloads"][workload]))
 
 
+SWEEP_N = (2048, 4096, 8192, 16384)
+
+
+def sweep_traffic(fetch_csv: str, write_csv: str):
+    """Traffic per N of an `--n-sweep` run under rocprofv3 --pmc FETCH_SIZE
+    (then WRITE_SIZE; KiB per dispatch): the sweep launches the attention
+    kernel three times per N, N in increasing order, so the k-th group of
+    three attention dispatches is the k-th N.  FETCH_SIZE is scaled x2 and
+    WRITE_SIZE x1, the factors a 1 GiB device copy calibrates."""
+    rows = {}
+    for name, path, counter, scale in (("fetch", fetch_csv, "FETCH_SIZE", 2.0),
+                                       ("write", write_csv, "WRITE_SIZE", 1.0)):
+        per = _pmc_rows(path)
+        attn = [c[counter] for (d, k), c in sorted(per.items()) if "fa_fwd" in k]
+        if len(attn) != 3 * len(SWEEP_N):
+            raise SystemExit("%s: %d attention dispatches, expected %d" % (path, len(attn),
+                                                                       3 * len(SWEEP_N)))
+        for i, N in enumerate(SWEEP_N):
+            three = sorted(attn[3 * i:3 * i + 3])
+            rows.setdefault(N, {})[name] = three[1] * 1024.0 * scale  # median launch, bytes
+    prev = None
+    for N in SWEEP_N:
+        qkv = 3 * 32 * N * 128 * 2
+        tot = rows[N]["fetch"] + rows[N]["write"]
+        slope = "" if prev is None else "%.2f" % (math.log2(tot / prev[1]) / math.log2(N / prev[0]))
+        print(json.dumps({"N": N, "fetched_MB": round(rows[N]["fetch"] / 1e6, 1),
+                          "x_qkv": round(rows[N]["fetch"] / qkv, 2),
+                          "written_MB": round(rows[N]["write"] / 1e6, 1),
+                          "total_MB": round(tot / 1e6, 1), "slope_vs_prev": slope}))
+        prev = (N, tot)
+    first, last = SWEEP_N[0], SWEEP_N[-1]
+    t0 = rows[first]["fetch"] + rows[first]["write"]
+    t1 = rows[last]["fetch"] + rows[last]["write"]
+    print(json.dumps({"overall_slope": round(math.log2(t1 / t0) / math.log2(last / first), 3)}))
+
+
 def n_sweep(torch, fa):
     """O(N) evidence: bf16 causal B=1 H=32 d=128 at N = 2048 .. 16384, seeded
-    N(0,1) inputs, two warm-up launches and one timed launch per N.  Under
-    rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE each N's dispatches are told apart
-    by their grid size (B*H*ceil(N/256) workgroups of 512 threads)."""
+    N(0,1) inputs, two warm-up launches and one timed launch per N, N in
+    increasing order (sweep_traffic reads the counters of each N's three
+    dispatches by that order)."""
     import numpy as np
-    for N in (2048, 4096, 8192, 16384):
+    for N in SWEEP_N:
         rng = np.random.default_rng(2000 + N)
         shape = (1, 32, N, 128)
         q, k, v = (torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(torch.bfloat16).cuda()
@@ -341,8 +377,7 @@ def n_sweep(torch, fa):
         ms = e0.elapsed_time(e1)
         flops = 2.0 * 32 * N * N * 128
         print(json.dumps({"sweep": "bf16 causal B=1 H=32 d=128", "N": N, "kernel_ms": round(ms, 4),
-                          "tflops": round(flops / ms / 1e9, 2),
-                          "grid_threads": 32 * ((N + 255) // 256) * 512}), flush=True)
+                          "tflops": round(flops / ms / 1e9, 2)}), flush=True)
 
 
 def bwd_bench(torch, fa, si, steps: int, warmup: int, w=None):
@@ -500,6 +535,10 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--record-traffic":
         # --record-traffic FETCH_CSV WRITE_CSV WORKLOAD "COMMAND"
         record_traffic(*sys.argv[2:6])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--sweep-traffic":
+        # --sweep-traffic FETCH_CSV WRITE_CSV (of two `--n-sweep` counter runs)
+        sweep_traffic(*sys.argv[2:4])
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)

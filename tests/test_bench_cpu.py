@@ -101,3 +101,30 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "exactly one GPU" in r.stderr and r.stdout == ""
+
+
+def test_sweep_traffic_groups_dispatches_by_order(tmp_path, capsys):
+    """--sweep-traffic: the k-th group of three attention dispatches is the
+    k-th N; other kernels in between are ignored; the median launch is used."""
+    import json as _json
+
+    def csv(path, counter, vals):
+        lines = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+        d = 0
+        for i, N in enumerate(bench.SWEEP_N):
+            d += 1
+            lines.append("%d,fill_kernel,%s,5" % (d, counter))
+            for j in range(3):
+                d += 1
+                lines.append("%d,fa_fwd16_kernel<2; 128; false>,%s,%s" % (d, counter, vals(i, j)))
+        path.write_text("\n".join(lines) + "\n")
+
+    f, w = tmp_path / "f.csv", tmp_path / "w.csv"
+    csv(f, "FETCH_SIZE", lambda i, j: 1000 * 4 ** i + j)   # median = 1000 * 4^i + 1
+    csv(w, "WRITE_SIZE", lambda i, j: 100 * 2 ** i)
+    bench.sweep_traffic(str(f), str(w))
+    out = [_json.loads(l) for l in capsys.readouterr().out.splitlines()]
+    assert [o["N"] for o in out[:-1]] == list(bench.SWEEP_N)
+    assert out[0]["fetched_MB"] == round((1000 + 1) * 1024 * 2 / 1e6, 1)
+    assert out[3]["written_MB"] == round(800 * 1024 / 1e6, 1)
+    assert 1.8 < out[-1]["overall_slope"] < 2.0
