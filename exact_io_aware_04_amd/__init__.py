@@ -3,7 +3,7 @@ gfx950 (MI355X).
 
 The functions named like the C ABI (``fa_fwd``, ``fa_fwd_gqa``, ``fa_fwd_fp8``, ``fa_bwd_gqa``, ``fa_decode``,
 ``fa_decode_workspace_bytes``, ``fa_decode_noalloc``, ``fa_bwd``, ``fa_fwd_record_tiles``,
-``fa_tile_shape``, ``fa_tile_map``, ``fa_status_string``, ``fa_last_error``,
+``fa_tile_shape``, ``fa_tile_map``, ``fa_fwd_schedule``, ``fa_status_string``, ``fa_last_error``,
 ``fa_probe_mfma``, ``fa_mfma_ceiling``) only marshal arguments: pointers are plain integers
 (device addresses, e.g. ``tensor.data_ptr()``), the stream is a hipStream_t
 handle (``torch.cuda.current_stream().cuda_stream``), and every step of the
@@ -76,6 +76,8 @@ def load():
     lib.fa_tile_shape.restype = i
     lib.fa_tile_map.argtypes = [i, i, i, i, i, vp]
     lib.fa_tile_map.restype = i
+    lib.fa_fwd_schedule.argtypes = [i, i, i, i, i, i, i, ip, ip, vp, ctypes.c_longlong]
+    lib.fa_fwd_schedule.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -176,6 +178,30 @@ def fa_tile_map(N: int, d: int, in_dtype: int, mask_kind: int, window: int):
         raise FaError(st, "fa_tile_map")
     flat = bytes(buf)
     return [list(flat[r * C:(r + 1) * C]) for r in range(R)]
+
+
+def fa_fwd_schedule(B: int, H: int, N: int, d: int, in_dtype: int, mask_kind: int,
+                    compute_units: int):
+    """Forward work order: a list with one entry per workgroup, each the
+    list of (batch*head, row tile) pairs it takes, in order."""
+    G, R = ctypes.c_int(0), ctypes.c_int(0)
+    lib = load()
+    st = lib.fa_fwd_schedule(B, H, N, d, in_dtype, mask_kind, compute_units,
+                             ctypes.byref(G), ctypes.byref(R), None, 0)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_schedule")
+    n = 2 * G.value * R.value
+    buf = (ctypes.c_int * n)()
+    st = lib.fa_fwd_schedule(B, H, N, d, in_dtype, mask_kind, compute_units,
+                             ctypes.byref(G), ctypes.byref(R), ctypes.cast(buf, ctypes.c_void_p), n)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_schedule")
+    flat = list(buf)
+    out = []
+    for g in range(G.value):
+        row = flat[2 * g * R.value:2 * (g + 1) * R.value]
+        out.append([(row[2 * k], row[2 * k + 1]) for k in range(R.value) if row[2 * k] >= 0])
+    return out
 
 
 def fa_status_string(status: int) -> str:

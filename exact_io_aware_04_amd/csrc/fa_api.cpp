@@ -166,19 +166,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   if (!(p.scale_log2 >= FLT_MIN)) p.scale_log2 = FLT_MIN;
   p.v_scale = v_scale;
   p.n_row_tiles = (N + fa_rows_per_wg(in_dtype, d) - 1) / fa_rows_per_wg(in_dtype, d);
-  p.xcd_split = (p.BH % 8 == 0) ? 1 : 0;
-  p.heavy_first = mask_kind != FA_MASK_NONE ? 1 : 0;
-  // Persistent launch of the 16-bit kernel: one workgroup per compute unit
-  // (fewer when there are fewer tiles), a multiple of the 8 groups when
-  // every XCD owns its own heads.
-  {
-    const long long total = (long long)p.BH * p.n_row_tiles;
-    p.n_groups = p.xcd_split ? 8 : 1;
-    long long g = std::min<long long>(total, device_cus());
-    g = std::max<long long>(p.n_groups, g / p.n_groups * p.n_groups);
-    p.wg_per_group = (int)(g / p.n_groups);
-    p.tiles_per_group = (int)(total / p.n_groups);
-  }
+  fa_fwd_plan(p, mask_kind, device_cus());
   hipError_t e = in_dtype == FA_DTYPE_E4M3
                      ? fa_launch_fwd8(out_dtype, d, p, (hipStream_t)stream)
                      : fa_launch_fwd(in_dtype, out_dtype, d, p, (hipStream_t)stream);
@@ -564,6 +552,49 @@ int fa_tile_map(int N, int d, int in_dtype, int mask_kind, int window, unsigned 
       out[(size_t)rb * C + kb] =
           (unsigned char)fa_classify(r0, r1, kb * bc, bc, N, mask_kind, window);
   }
+  return ok();
+}
+
+int fa_fwd_schedule(int B, int H, int N, int d, int in_dtype, int mask_kind, int compute_units,
+                    int* n_workgroups, int* max_tiles, int* out, long long out_len) {
+  if (!n_workgroups || !max_tiles) return fail(FA_ERR_INVALID_ARG, "null output pointer");
+  if (B < 1 || H < 1 || N < 1 || N >= (1 << 30) || compute_units < 1)
+    return fail(FA_ERR_INVALID_ARG, "bad sizes B=%d H=%d N=%d compute_units=%d", B, H, N,
+                compute_units);
+  if (!valid_dtype(in_dtype) && in_dtype != FA_DTYPE_E4M3)
+    return fail(FA_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL && mask_kind != FA_MASK_SLIDING)
+    return fail(FA_ERR_INVALID_ARG, "unknown mask_kind %d", mask_kind);
+  if (!fa_head_dim_built(in_dtype, d))
+    return fail(FA_ERR_UNSUPPORTED, "head dim %d not built for in_dtype %d", d, in_dtype);
+  const int rows = fa_rows_per_wg(in_dtype, d);
+  const long long T = (N + rows - 1) / rows;
+  if ((long long)B * H * T >= (1LL << 31))
+    return fail(FA_ERR_INVALID_ARG, "B*H*row tiles beyond int range");
+  FaFwdParams p{};
+  p.BH = B * H;
+  p.n_row_tiles = (int)T;
+  fa_fwd_plan(p, mask_kind, compute_units);
+  const bool persistent = fa_fwd_persistent(in_dtype, d);
+  const long long G = persistent ? (long long)p.n_groups * p.wg_per_group : (long long)p.BH * T;
+  const long long R = persistent ? (p.tiles_per_group + p.wg_per_group - 1) / p.wg_per_group : 1;
+  *n_workgroups = (int)G;
+  *max_tiles = (int)R;
+  if (!out) return ok();
+  if (out_len < 2 * G * R)
+    return fail(FA_ERR_INVALID_ARG, "out holds %lld ints, the schedule needs %lld", out_len,
+                2 * G * R);
+  for (long long g = 0; g < G; ++g)
+    for (long long k = 0; k < R; ++k) {
+      int bh = -1, qt = -1;
+      if (persistent) {
+        if (!fa_persist_tile_of(p, (int)g, (int)k, &bh, &qt)) bh = qt = -1;
+      } else {
+        fa_plain_tile_of(p, (int)g, &bh, &qt);
+      }
+      out[2 * (g * R + k)] = bh;
+      out[2 * (g * R + k) + 1] = qt;
+    }
   return ok();
 }
 

@@ -298,7 +298,9 @@ __device__ __forceinline__ void matrix_phase(fa_f32x16 (&acc)[D / 32], fa_f32x16
 // groups in opposite phases.
 //
 // Persistent: one workgroup per compute unit walks its list of row tiles
-// (persist_tile).  The K/V blocks of consecutive tiles form one stream
+// (fa_persist_tile_of; under a causal mask or none, the tiles an XCD runs
+// together are row tiles of one head, so its L2 serves their common key and
+// value blocks once from HBM).  The K/V blocks of consecutive tiles form one stream
 // through the LDS rings: the first two blocks of the next tile are loaded
 // during the last two steps of the current one, so a new tile starts with
 // its first blocks in LDS and no workgroup launch in between.

@@ -11,51 +11,19 @@
 
 namespace {
 
-// Work item of this workgroup: (batch*head, first query row).
+// Work item of this workgroup in the plain launch: (batch*head, first row).
 template <int ROWS_WG>
 __device__ __forceinline__ void work_item(const FaFwdParams& p, int& bh, int& q0) {
-  const int T = p.n_row_tiles;
-  const int b = blockIdx.x;
-  int rank;
-  if (p.xcd_split) {
-    const int hpx = p.BH >> 3;  // heads per XCD
-    const int s = b >> 3;
-    bh = (b & 7) * hpx + s % hpx;
-    rank = s / hpx;
-  } else {
-    bh = b % p.BH;
-    rank = b / p.BH;
-  }
-  const int qt = p.heavy_first ? (T - 1 - rank) : rank;
+  int qt;
+  fa_plain_tile_of(p, blockIdx.x, &bh, &qt);
   q0 = qt * ROWS_WG;
 }
 
-// Tile k of a persistent workgroup: false when it has no k-th tile.  Within
-// its group (blockIdx mod n_groups: the XCD when every XCD owns BH / 8
-// heads) the tiles are numbered s = 0 .. tiles_per_group-1 as the plain
-// launch orders its workgroups (longest first under a mask, heads fastest),
-// and the group's J workgroups take them in a snake: round r covers s = rJ
-// .. rJ+J-1, forwards on even rounds and backwards on odd ones, so a
-// workgroup that drew a long tile next draws a short one.  Once a
-// workgroup's s passes the end, every later one does too.
+// Tile k of this persistent workgroup (order: fa_persist_tile_of).
 __device__ __forceinline__ bool persist_tile(const FaFwdParams& p, int k, int& bh, int& q0,
                                              int rows_wg) {
-  const int g = blockIdx.x;
-  const int x = g % p.n_groups, j = g / p.n_groups;
-  const int J = p.wg_per_group;
-  const int s = (k & 1) ? (k + 1) * J - 1 - j : k * J + j;
-  if (s >= p.tiles_per_group) return false;
-  const int T = p.n_row_tiles;
-  int rank;
-  if (p.n_groups > 1) {
-    const int hpx = p.BH / p.n_groups;  // heads per group
-    bh = x * hpx + s % hpx;
-    rank = s / hpx;
-  } else {
-    bh = s % p.BH;
-    rank = s / p.BH;
-  }
-  const int qt = p.heavy_first ? (T - 1 - rank) : rank;
+  int qt;
+  if (!fa_persist_tile_of(p, blockIdx.x, k, &bh, &qt)) return false;
   q0 = qt * rows_wg;
   return true;
 }

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "tile_class.h"
+
 struct FaFwdParams {
   const void* q;
   const void* k;
@@ -30,6 +32,7 @@ struct FaFwdParams {
   int n_groups;
   int wg_per_group;
   int tiles_per_group;
+  int head_major;         // 1: a group's row tiles numbered head by head
 };
 
 // Backward pass (fa_bwd.hip).
@@ -119,6 +122,97 @@ constexpr int fa_keys_per_block(int in_dtype, int d) {
 // query rows per workgroup for an input dtype code (0 = f32) and head dim
 constexpr int fa_rows_per_wg(int in_dtype, int d) {
   return (in_dtype == 0 ? FA_WAVES_32 : d == 256 ? FA_WAVES_WIDE : FA_WAVES_16) * FA_ROW_BLOCK;
+}
+
+// The forward launch with one persistent workgroup per compute unit: the
+// f16/bf16 kernel at d = 64 and 128.  Every other forward kernel is launched
+// with one workgroup per row tile.
+constexpr bool fa_fwd_persistent(int in_dtype, int d) {
+  return (in_dtype == 1 || in_dtype == 2) && d <= 128;
+}
+
+// Work order of the forward, shared by the host (launch plan, schedule
+// export) and the kernels.
+//
+// Plain launch: workgroup b takes one row tile.  With every XCD owning its
+// own BH / 8 heads (xcd_split; blockIdx b runs on XCD b mod 8) the tiles
+// of XCD x are numbered s = b / 8 with heads fastest; otherwise s = b over
+// all heads.  Rank s / heads is the tile's place in launch order; under a
+// mask the longest row tiles (highest qt) go first.
+FA_HD void fa_plain_tile_of(const FaFwdParams& p, int b, int* bh, int* qt) {
+  const int T = p.n_row_tiles;
+  int rank;
+  if (p.xcd_split) {
+    const int hpx = p.BH >> 3;
+    const int s = b >> 3;
+    *bh = (b & 7) * hpx + s % hpx;
+    rank = s / hpx;
+  } else {
+    *bh = b % p.BH;
+    rank = b / p.BH;
+  }
+  *qt = p.heavy_first ? (T - 1 - rank) : rank;
+}
+
+// Persistent launch: tile k of workgroup g, false when g has no k-th tile.
+// Within its group (g mod n_groups: the XCD when every XCD owns BH / 8
+// heads) the tiles are numbered s = 0 .. tiles_per_group-1 and the group's
+// J workgroups take them in a snake: round r covers s = rJ .. rJ+J-1,
+// forwards on even rounds and backwards on odd ones, so a workgroup that
+// drew a long tile next draws a short one.  Numbering (row tiles longest
+// first under a mask):
+//   head_major = 0: heads fastest, s = rank * heads + head.  Every prefix
+//     is sorted longest first, which balances any mix of tile lengths.
+//   head_major = 1: row tiles fastest, s = head * T + rank.  The J tiles of
+//     a round share one head (or whole heads when T < J), start together and
+//     stream the same key/value blocks, so the group's L2 serves most of
+//     them; balanced when every pair of snake rounds pairs rank t with rank
+//     2J-1-t of equal-sum lengths (causal with T a multiple or divisor of 2J)
+//     or when all tiles have one length (no mask).
+// Once a workgroup's s passes the end, every later one does too.
+FA_HD bool fa_persist_tile_of(const FaFwdParams& p, int g, int k, int* bh, int* qt) {
+  const int x = g % p.n_groups, j = g / p.n_groups;
+  const int J = p.wg_per_group;
+  const int s = (k & 1) ? (k + 1) * J - 1 - j : k * J + j;
+  if (s >= p.tiles_per_group) return false;
+  const int T = p.n_row_tiles;
+  const int hpg = p.BH / p.n_groups;  // heads per group
+  int head, rank;
+  if (p.head_major) {
+    head = s / T;
+    rank = s - head * T;
+  } else {
+    rank = s / hpg;
+    head = s - rank * hpg;
+  }
+  *bh = x * hpg + head;
+  *qt = p.heavy_first ? (T - 1 - rank) : rank;
+  return true;
+}
+
+// Plan of a forward launch on a device with `cus` compute units: sets
+// xcd_split, heavy_first and, for the persistent launch, one workgroup per
+// compute unit (fewer when there are fewer tiles), a multiple of the 8
+// groups when every XCD owns its own heads, and the numbering.  Requires
+// BH and n_row_tiles.
+inline void fa_fwd_plan(FaFwdParams& p, int mask_kind, int cus) {
+  p.xcd_split = (p.BH % 8 == 0) ? 1 : 0;
+  p.heavy_first = mask_kind != FA_MASKK_NONE ? 1 : 0;
+  const long long total = (long long)p.BH * p.n_row_tiles;
+  p.n_groups = p.xcd_split ? 8 : 1;
+  long long g = total < cus ? total : cus;
+  g = g / p.n_groups * p.n_groups;
+  if (g < p.n_groups) g = p.n_groups;
+  p.wg_per_group = (int)(g / p.n_groups);
+  p.tiles_per_group = (int)(total / p.n_groups);
+  // Head by head when that keeps the snake balanced: tiles of one length
+  // (no mask), or causal lengths 1..T units with T and 2J dividing one
+  // another (snake rounds then pair rank t with rank 2J-1-t).  Sliding
+  // windows keep heads fastest: their short tiles sit at each head's start
+  // and must spread over all workgroups.
+  const long long T = p.n_row_tiles, J2 = 2LL * p.wg_per_group;
+  p.head_major = mask_kind == FA_MASKK_NONE ||
+                 (mask_kind == FA_MASKK_CAUSAL && (T % J2 == 0 || J2 % T == 0));
 }
 
 // head dims built for an input dtype code: 64 and 128, 256 for f16/bf16,

@@ -1,0 +1,131 @@
+"""The forward's work order (fa_fwd_schedule, host only): every row tile is
+taken exactly once, the persistent workgroups' loads are balanced, and under
+the head-by-head numbering the tiles a group runs together share one head's
+keys and values.
+
+The order decides speed and HBM traffic only (each tile's output depends on
+its own rows), so these properties are checked here on the host; the GPU
+parity tests check the outputs the same launches produce.
+"""
+import ctypes
+
+import pytest
+
+import exact_io_aware_04_amd as fa
+
+BF16, F16, F32, E4M3 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_F16, fa.FA_DTYPE_F32, fa.FA_DTYPE_E4M3
+NONE, CAUSAL, SLIDING = fa.FA_MASK_NONE, fa.FA_MASK_CAUSAL, fa.FA_MASK_SLIDING
+
+# (B, H, N, d, dtype, mask, window): the five benchmark workloads, the N
+# sweep, a grouped-query case, the 8-bit and wide kernels, ragged sizes
+CASES = [
+    (1, 1, 128, 64, F32, NONE, 0),
+    (16, 12, 1024, 64, F16, NONE, 0),
+    (4, 16, 2048, 128, BF16, CAUSAL, 0),
+    (1, 32, 16384, 128, BF16, CAUSAL, 0),
+    (1, 32, 32768, 128, BF16, SLIDING, 4096),
+    (1, 32, 2048, 128, BF16, CAUSAL, 0),
+    (1, 32, 4096, 128, BF16, CAUSAL, 0),
+    (1, 32, 8192, 128, BF16, CAUSAL, 0),
+    (2, 8, 12288, 128, BF16, CAUSAL, 0),
+    (1, 32, 16384, 128, E4M3, CAUSAL, 0),
+    (1, 16, 16384, 256, BF16, CAUSAL, 0),
+    (3, 5, 1000, 64, F16, CAUSAL, 0),
+    (3, 5, 1000, 128, BF16, SLIDING, 300),
+    (1, 1, 300, 128, BF16, CAUSAL, 0),
+]
+
+
+def _rows(d, dtype):
+    """Query rows per row tile (the E4M3 kernel tiles like bf16)."""
+    return fa.fa_tile_shape(d, BF16 if dtype == E4M3 else dtype)[0]
+
+
+def key_blocks(qt, rows, N, mask, window, bc=64):
+    """Key blocks a row tile visits (mask range of its rows)."""
+    r0, r1 = qt * rows, min(N, (qt + 1) * rows)
+    hi = -(-N // bc) if mask == NONE else -(-r1 // bc)
+    lo = 0 if mask != SLIDING else max(0, r0 - window + 1) // bc
+    return hi - lo
+
+
+def persistent(dtype, d):
+    return dtype in (F16, BF16) and d <= 128
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b%dh%dn%dd%d_t%d_m%d" % c[:6])
+@pytest.mark.parametrize("cus", [256, 80])
+def test_every_row_tile_exactly_once(case, cus):
+    B, H, N, d, dt, mask, window = case
+    sched = fa.fa_fwd_schedule(B, H, N, d, dt, mask, cus)
+    rows = _rows(d, dt)
+    T = -(-N // rows)
+    got = sorted(t for wg in sched for t in wg)
+    assert got == sorted((bh, qt) for bh in range(B * H) for qt in range(T))
+    if persistent(dt, d):
+        assert len(sched) <= cus
+        # a multiple of the 8 XCD groups when every XCD owns its own heads
+        if (B * H) % 8 == 0:
+            assert len(sched) % 8 == 0
+    else:
+        assert len(sched) == B * H * T and all(len(wg) == 1 for wg in sched)
+
+
+@pytest.mark.parametrize("case", [c for c in CASES if persistent(c[4], c[3]) and c[1] * c[0] % 8 == 0],
+                         ids=lambda c: "b%dh%dn%dd%d_m%d" % (c[0], c[1], c[2], c[3], c[5]))
+def test_persistent_loads_balanced(case):
+    """Per-workgroup work (key blocks visited, at least two per tile, plus
+    one block's worth of tile start and output) within 3 % of the mean when
+    every workgroup takes an even number of tiles (whole snake round
+    pairs); the five-case list holds such cases for each numbering."""
+    B, H, N, d, dt, mask, window = case
+    sched = fa.fa_fwd_schedule(B, H, N, d, dt, mask, 256)
+    rows = _rows(d, dt)
+    load = [sum(max(2, key_blocks(qt, rows, N, mask, window)) + 1 for _, qt in wg) for wg in sched]
+    mean = sum(load) / len(load)
+    if all(len(wg) % 2 == 0 for wg in sched):
+        assert max(load) <= 1.03 * mean, (max(load), mean)
+
+
+@pytest.mark.parametrize("N,heads_per_round", [(16384, 1), (8192, 1), (4096, 2), (2048, 4)])
+def test_head_major_rounds_share_heads(N, heads_per_round):
+    """Causal B=1 H=32 d=128 on 256 compute units: each XCD group's 32
+    workgroups take whole rounds of one head's row tiles (or of
+    32 / T heads when a head has T < 32 tiles), so the tiles running
+    together stream the same key/value blocks."""
+    sched = fa.fa_fwd_schedule(1, 32, N, 128, BF16, CAUSAL, 256)
+    G = len(sched)
+    assert G == 256
+    R = max(len(wg) for wg in sched)
+    for x in range(8):
+        members = [sched[g] for g in range(x, G, 8)]
+        for k in range(R):
+            heads = {wg[k][0] for wg in members if k < len(wg)}
+            assert len(heads) <= heads_per_round
+            assert all(h // 4 == x for h in heads)  # the group's own heads
+
+
+def test_sliding_keeps_heads_fastest():
+    """Sliding windows number heads fastest: the short tiles at each head's
+    start land in the last rounds, spread over every workgroup."""
+    sched = fa.fa_fwd_schedule(1, 32, 32768, 128, BF16, SLIDING, 256)
+    first = [wg[0] for wg in sched]
+    assert len({bh for bh, _ in first}) == 32
+    assert all(qt >= 120 for _, qt in first)
+
+
+def test_schedule_rejects_bad_arguments():
+    lib = fa.load()
+    G, R = ctypes.c_int(0), ctypes.c_int(0)
+    g, r = ctypes.byref(G), ctypes.byref(R)
+    assert lib.fa_fwd_schedule(0, 1, 10, 128, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 10, 128, BF16, 7, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 10, 128, BF16, 0, 0, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 10, 100, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_fwd_schedule(1, 1, 10, 128, 9, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 10, 128, BF16, 0, 256, None, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 1 << 30, 128, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 2, 1000, 128, BF16, 1, 256, g, r, None, 0) == fa.FA_OK
+    buf = (ctypes.c_int * 4)()
+    assert lib.fa_fwd_schedule(1, 2, 1000, 128, BF16, 1, 256, g, r,
+                               ctypes.cast(buf, ctypes.c_void_p), 4) == fa.FA_ERR_INVALID_ARG
