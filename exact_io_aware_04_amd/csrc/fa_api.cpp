@@ -555,12 +555,15 @@ int fa_tile_map(int N, int d, int in_dtype, int mask_kind, int window, unsigned 
   return ok();
 }
 
-int fa_fwd_schedule(int B, int H, int N, int d, int in_dtype, int mask_kind, int compute_units,
-                    int* n_workgroups, int* max_tiles, int* out, long long out_len) {
+int fa_fwd_schedule(int B, int H, int H_kv, int N, int d, int in_dtype, int mask_kind,
+                    int compute_units, int* n_workgroups, int* max_tiles, int* out,
+                    long long out_len) {
   if (!n_workgroups || !max_tiles) return fail(FA_ERR_INVALID_ARG, "null output pointer");
   if (B < 1 || H < 1 || N < 1 || N >= (1 << 30) || compute_units < 1)
     return fail(FA_ERR_INVALID_ARG, "bad sizes B=%d H=%d N=%d compute_units=%d", B, H, N,
                 compute_units);
+  if (H_kv < 1 || H % H_kv != 0)
+    return fail(FA_ERR_INVALID_ARG, "H=%d is not a multiple of H_kv=%d", H, H_kv);
   if (!valid_dtype(in_dtype) && in_dtype != FA_DTYPE_E4M3)
     return fail(FA_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
   if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL && mask_kind != FA_MASK_SLIDING)
@@ -573,6 +576,7 @@ int fa_fwd_schedule(int B, int H, int N, int d, int in_dtype, int mask_kind, int
     return fail(FA_ERR_INVALID_ARG, "B*H*row tiles beyond int range");
   FaFwdParams p{};
   p.BH = B * H;
+  p.kv_group = H / H_kv;
   p.n_row_tiles = (int)T;
   fa_fwd_plan(p, mask_kind, compute_units);
   const bool persistent = fa_fwd_persistent(in_dtype, d);

@@ -32,7 +32,9 @@ struct FaFwdParams {
   int n_groups;
   int wg_per_group;
   int tiles_per_group;
-  int head_major;         // 1: a group's row tiles numbered head by head
+  int kv_major;           // 1: a group's row tiles numbered K/V head by K/V head
+  int kv_share;           // query heads of one K/V head within a group (numbered
+                          // fastest under kv_major)
 };
 
 // Backward pass (fa_bwd.hip).
@@ -161,14 +163,17 @@ FA_HD void fa_plain_tile_of(const FaFwdParams& p, int b, int* bh, int* qt) {
 // forwards on even rounds and backwards on odd ones, so a workgroup that
 // drew a long tile next draws a short one.  Numbering (row tiles longest
 // first under a mask):
-//   head_major = 0: heads fastest, s = rank * heads + head.  Every prefix
-//     is sorted longest first, which balances any mix of tile lengths.
-//   head_major = 1: row tiles fastest, s = head * T + rank.  The J tiles of
-//     a round share one head (or whole heads when T < J), start together and
-//     stream the same key/value blocks, so the group's L2 serves most of
-//     them; balanced when every pair of snake rounds pairs rank t with rank
-//     2J-1-t of equal-sum lengths (causal with T a multiple or divisor of 2J)
-//     or when all tiles have one length (no mask).
+//   kv_major = 0: heads fastest, s = rank * heads + head.  Every prefix is
+//     sorted longest first, which balances any mix of tile lengths.
+//   kv_major = 1: the group's heads form sets of G = kv_share query heads
+//     that read one K/V head; s = set * G T + rank * G + head in set.  The
+//     J tiles of a round then read one K/V head (or whole sets when G T <
+//     J), start together and stream the same key/value blocks, so the
+//     group's L2 serves most of them from one fetch; the rank changes every
+//     G tiles, so a round also holds tiles of similar length.  Balanced when
+//     every pair of snake rounds pairs position t with 2J-1-t at equal
+//     summed length: no mask, or causal with G T a multiple or divisor of
+//     2J.  (G = heads per group gives the kv_major = 0 order.)
 // Once a workgroup's s passes the end, every later one does too.
 FA_HD bool fa_persist_tile_of(const FaFwdParams& p, int g, int k, int* bh, int* qt) {
   const int x = g % p.n_groups, j = g / p.n_groups;
@@ -178,9 +183,11 @@ FA_HD bool fa_persist_tile_of(const FaFwdParams& p, int g, int k, int* bh, int* 
   const int T = p.n_row_tiles;
   const int hpg = p.BH / p.n_groups;  // heads per group
   int head, rank;
-  if (p.head_major) {
-    head = s / T;
-    rank = s - head * T;
+  if (p.kv_major) {
+    const int G = p.kv_share, per = G * T;
+    const int set = s / per, r = s - set * per;
+    rank = r / G;
+    head = set * G + (r - rank * G);
   } else {
     rank = s / hpg;
     head = s - rank * hpg;
@@ -194,7 +201,7 @@ FA_HD bool fa_persist_tile_of(const FaFwdParams& p, int g, int k, int* bh, int* 
 // xcd_split, heavy_first and, for the persistent launch, one workgroup per
 // compute unit (fewer when there are fewer tiles), a multiple of the 8
 // groups when every XCD owns its own heads, and the numbering.  Requires
-// BH and n_row_tiles.
+// BH, kv_group and n_row_tiles.
 inline void fa_fwd_plan(FaFwdParams& p, int mask_kind, int cus) {
   p.xcd_split = (p.BH % 8 == 0) ? 1 : 0;
   p.heavy_first = mask_kind != FA_MASKK_NONE ? 1 : 0;
@@ -205,14 +212,23 @@ inline void fa_fwd_plan(FaFwdParams& p, int mask_kind, int cus) {
   if (g < p.n_groups) g = p.n_groups;
   p.wg_per_group = (int)(g / p.n_groups);
   p.tiles_per_group = (int)(total / p.n_groups);
-  // Head by head when that keeps the snake balanced: tiles of one length
-  // (no mask), or causal lengths 1..T units with T and 2J dividing one
-  // another (snake rounds then pair rank t with rank 2J-1-t).  Sliding
-  // windows keep heads fastest: their short tiles sit at each head's start
-  // and must spread over all workgroups.
-  const long long T = p.n_row_tiles, J2 = 2LL * p.wg_per_group;
-  p.head_major = mask_kind == FA_MASKK_NONE ||
-                 (mask_kind == FA_MASKK_CAUSAL && (T % J2 == 0 || J2 % T == 0));
+  // Query heads of a group that read one K/V head: the group's heads start
+  // at a multiple of hpg and K/V heads change every kv_group heads, so sets
+  // of gcd(kv_group, hpg) consecutive heads each read one K/V head.
+  int a = p.kv_group, b = p.BH / p.n_groups;
+  while (b) {
+    const int t = a % b;
+    a = b;
+    b = t;
+  }
+  p.kv_share = a;
+  // K/V head by K/V head when that keeps the snake balanced: tiles of one
+  // length (no mask), or causal lengths with G T and 2J dividing one
+  // another.  Sliding windows keep heads fastest: their short tiles sit at
+  // each head's start and must spread over all workgroups.
+  const long long GT = (long long)p.kv_share * p.n_row_tiles, J2 = 2LL * p.wg_per_group;
+  p.kv_major = mask_kind == FA_MASKK_NONE ||
+               (mask_kind == FA_MASKK_CAUSAL && (GT % J2 == 0 || J2 % GT == 0));
 }
 
 // head dims built for an input dtype code: 64 and 128, 256 for f16/bf16,

@@ -15,6 +15,7 @@ Tolerances: O max-abs <= 1e-5 (fp32 inputs) / 1e-2 (bf16, fp16; plus half
 an ulp of the output dtype when O is stored in it); lse <= 1e-3.
 """
 import math
+import time
 
 import numpy as np
 import pytest
@@ -103,7 +104,10 @@ def test_workload_whole_tensor(w):
         assert o16.dtype == dt
         o16, lse16 = o16.cpu(), lse16.cpu()
     say("workload whole", w.name, "oracle")
+    t0 = time.perf_counter()
     o_ref, lse_ref = oracle.attention(q, k, v, w.scale, w.mask, w.window)
+    say("%s oracle: %.2f s on %d host threads" % (w.name, time.perf_counter() - t0,
+                                                  oracle.num_threads()))
     eo, el = compare(o32, lse32, o_ref, lse_ref, dt, w.name + " fp32-out")
     say("%s fp32-out: max|dO| %.3g max|dlse| %.3g" % (w.name, eo, el))
     if dt != torch.float32:

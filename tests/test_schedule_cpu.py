@@ -34,6 +34,13 @@ CASES = [
     (3, 5, 1000, 128, BF16, SLIDING, 300),
     (1, 1, 300, 128, BF16, CAUSAL, 0),
 ]
+# with H_kv: every case with its own key/value heads, and shared ones
+ALL = [c + (c[1],) for c in CASES] + [CASES[i] + (hkv,) for i, hkv in
+                                      [(3, 8), (3, 1), (2, 4), (2, 1), (11, 1), (7, 4)]]
+
+
+def case_id(c):
+    return "b%dh%dkv%dn%dd%d_t%d_m%d" % (c[0], c[1], c[7], c[2], c[3], c[4], c[5])
 
 
 def _rows(d, dtype):
@@ -53,11 +60,11 @@ def persistent(dtype, d):
     return dtype in (F16, BF16) and d <= 128
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "b%dh%dn%dd%d_t%d_m%d" % c[:6])
+@pytest.mark.parametrize("case", ALL, ids=case_id)
 @pytest.mark.parametrize("cus", [256, 80])
 def test_every_row_tile_exactly_once(case, cus):
-    B, H, N, d, dt, mask, window = case
-    sched = fa.fa_fwd_schedule(B, H, N, d, dt, mask, cus)
+    B, H, N, d, dt, mask, window, H_kv = case
+    sched = fa.fa_fwd_schedule(B, H, N, d, dt, mask, cus, H_kv=H_kv)
     rows = _rows(d, dt)
     T = -(-N // rows)
     got = sorted(t for wg in sched for t in wg)
@@ -71,15 +78,15 @@ def test_every_row_tile_exactly_once(case, cus):
         assert len(sched) == B * H * T and all(len(wg) == 1 for wg in sched)
 
 
-@pytest.mark.parametrize("case", [c for c in CASES if persistent(c[4], c[3]) and c[1] * c[0] % 8 == 0],
-                         ids=lambda c: "b%dh%dn%dd%d_m%d" % (c[0], c[1], c[2], c[3], c[5]))
+@pytest.mark.parametrize("case", [c for c in ALL if persistent(c[4], c[3]) and c[1] * c[0] % 8 == 0],
+                         ids=case_id)
 def test_persistent_loads_balanced(case):
     """Per-workgroup work (key blocks visited, at least two per tile, plus
     one block's worth of tile start and output) within 3 % of the mean when
     every workgroup takes an even number of tiles (whole snake round
     pairs); the five-case list holds such cases for each numbering."""
-    B, H, N, d, dt, mask, window = case
-    sched = fa.fa_fwd_schedule(B, H, N, d, dt, mask, 256)
+    B, H, N, d, dt, mask, window, H_kv = case
+    sched = fa.fa_fwd_schedule(B, H, N, d, dt, mask, 256, H_kv=H_kv)
     rows = _rows(d, dt)
     load = [sum(max(2, key_blocks(qt, rows, N, mask, window)) + 1 for _, qt in wg) for wg in sched]
     mean = sum(load) / len(load)
@@ -87,20 +94,27 @@ def test_persistent_loads_balanced(case):
         assert max(load) <= 1.03 * mean, (max(load), mean)
 
 
-@pytest.mark.parametrize("N,heads_per_round", [(16384, 1), (8192, 1), (4096, 2), (2048, 4)])
-def test_head_major_rounds_share_heads(N, heads_per_round):
+@pytest.mark.parametrize("N,H_kv,kv_per_round,heads_per_round",
+                         [(16384, 32, 1, 1), (8192, 32, 1, 1), (4096, 32, 2, 2), (2048, 32, 4, 4),
+                          (16384, 8, 1, 4), (16384, 1, 1, 4), (2048, 8, 1, 4)])
+def test_rounds_share_key_value_heads(N, H_kv, kv_per_round, heads_per_round):
     """Causal B=1 H=32 d=128 on 256 compute units: each XCD group's 32
-    workgroups take whole rounds of one head's row tiles (or of
-    32 / T heads when a head has T < 32 tiles), so the tiles running
-    together stream the same key/value blocks."""
-    sched = fa.fa_fwd_schedule(1, 32, N, 128, BF16, CAUSAL, 256)
+    workgroups take whole rounds of tiles that read one key/value head (or
+    32 / (G T) of them when its G query heads have fewer than 32 tiles in
+    all), so the tiles running together stream the same key/value blocks;
+    the query heads of a shared key/value head alternate fastest, so a round
+    holds 32 / G row tiles of each."""
+    g = 32 // H_kv
+    sched = fa.fa_fwd_schedule(1, 32, N, 128, BF16, CAUSAL, 256, H_kv=H_kv)
     G = len(sched)
     assert G == 256
     R = max(len(wg) for wg in sched)
     for x in range(8):
-        members = [sched[g] for g in range(x, G, 8)]
+        members = [sched[gi] for gi in range(x, G, 8)]
         for k in range(R):
-            heads = {wg[k][0] for wg in members if k < len(wg)}
+            tiles = [wg[k] for wg in members if k < len(wg)]
+            heads = {bh for bh, _ in tiles}
+            assert len({bh // g for bh in heads}) <= kv_per_round
             assert len(heads) <= heads_per_round
             assert all(h // 4 == x for h in heads)  # the group's own heads
 
@@ -118,14 +132,16 @@ def test_schedule_rejects_bad_arguments():
     lib = fa.load()
     G, R = ctypes.c_int(0), ctypes.c_int(0)
     g, r = ctypes.byref(G), ctypes.byref(R)
-    assert lib.fa_fwd_schedule(0, 1, 10, 128, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 1, 10, 128, BF16, 7, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 1, 10, 128, BF16, 0, 0, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 1, 10, 100, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_UNSUPPORTED
-    assert lib.fa_fwd_schedule(1, 1, 10, 128, 9, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 1, 10, 128, BF16, 0, 256, None, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 1, 1 << 30, 128, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 2, 1000, 128, BF16, 1, 256, g, r, None, 0) == fa.FA_OK
+    assert lib.fa_fwd_schedule(0, 1, 1, 10, 128, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 1, 10, 128, BF16, 7, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 1, 10, 128, BF16, 0, 0, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 1, 10, 100, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_fwd_schedule(1, 1, 1, 10, 128, 9, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 1, 10, 128, BF16, 0, 256, None, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 1, 1 << 30, 128, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 4, 3, 10, 128, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 4, 0, 10, 128, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 2, 2, 1000, 128, BF16, 1, 256, g, r, None, 0) == fa.FA_OK
     buf = (ctypes.c_int * 4)()
-    assert lib.fa_fwd_schedule(1, 2, 1000, 128, BF16, 1, 256, g, r,
+    assert lib.fa_fwd_schedule(1, 2, 2, 1000, 128, BF16, 1, 256, g, r,
                                ctypes.cast(buf, ctypes.c_void_p), 4) == fa.FA_ERR_INVALID_ARG
