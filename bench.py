@@ -48,10 +48,21 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "e4m3": 5033.2}
 METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak (bf16 causal, N=16384, d=128)"
 METRIC_FP8 = "attention fwd TFLOP/s + % E4M3 MFMA peak (e4m3 causal, N=16384, d=128)"
-KERNEL_SOURCES = ["exact_io_aware_04_amd/csrc/fa_fwd.hip", "exact_io_aware_04_amd/csrc/fa_fwd8.hip",
-                  "exact_io_aware_04_amd/csrc/fa_fwd_common.h", "exact_io_aware_04_amd/csrc/fa_device.h",
+# Sources a forward workload's kernel is built from: its kernel file (8-bit
+# inputs: fa_fwd8.hip, else fa_fwd.hip) and the shared ones.
+SHARED_SOURCES = ["exact_io_aware_04_amd/csrc/fa_fwd_common.h", "exact_io_aware_04_amd/csrc/fa_device.h",
                   "exact_io_aware_04_amd/csrc/fa_kernels.h", "exact_io_aware_04_amd/csrc/tile_class.h",
                   "exact_io_aware_04_amd/csrc/fa_api.cpp"]
+KERNEL_SOURCES = ["exact_io_aware_04_amd/csrc/fa_fwd.hip", "exact_io_aware_04_amd/csrc/fa_fwd8.hip"] + SHARED_SOURCES
+
+
+def kernel_sources(w=None):
+    """Source files of workload w's kernel (all forward sources for None)."""
+    if w is None:
+        return KERNEL_SOURCES
+    main = "exact_io_aware_04_amd/csrc/fa_fwd8.hip" if w.dtype == "e4m3" else \
+        "exact_io_aware_04_amd/csrc/fa_fwd.hip"
+    return [main] + SHARED_SOURCES
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.json")
 
 
@@ -105,11 +116,11 @@ def code_text(src: str) -> str:
     return "".join(out)
 
 
-def kernel_source_hash() -> str:
-    """SHA-256 of the kernel sources' code text (comments and layout
-    ignored)."""
+def kernel_source_hash(w=None) -> str:
+    """SHA-256 of the code text (comments and layout ignored) of workload
+    w's kernel sources (all forward sources for None)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in kernel_sources(w):
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             h.update(code_text(f.read()).encode("utf-8"))
         h.update(b"\0")
@@ -148,16 +159,14 @@ def algorithmic_bytes(w) -> int:
 
 def load_traffic(w):
     """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel sources and this workload."""
+    taken on this workload with the current sources of its kernel."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_src_sha256") != kernel_source_hash():
-        return None
     ent = rec.get("workloads", {}).get(w.name)
-    if not ent:
+    if not ent or ent.get("kernel_src_sha256") != kernel_source_hash(w):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -300,10 +309,11 @@ def record_traffic(fetch_csv: str, write_csv: str, workload: str, command: str):
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-    if rec.get("kernel_src_sha256") != kernel_source_hash():
-        rec = {"kernel_src_sha256": kernel_source_hash(), "workloads": {}}
+    rec.setdefault("workloads", {})
+    rec.pop("kernel_src_sha256", None)
     hbm = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
     rec["workloads"][workload] = {
+        "kernel_src_sha256": kernel_source_hash(w),
         "fetch": out["fetch"], "write": out["write"], "hbm_bytes_per_launch": round(hbm),
         "algorithmic_bytes": algorithmic_bytes(w), "ratio_to_algorithmic": hbm / algorithmic_bytes(w),
         "command": command}

@@ -11,9 +11,12 @@
 // v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32), twice the rate of the
 // 16-bit products.
 //
-// Work decomposition, ping-pong of the two wavefronts of a SIMD, tile
-// classes and work order are those of fa_fwd16_kernel (fa_fwd.hip); the K/V
-// rings have four slots (8 KB blocks).
+// Ping-pong of the two wavefronts of a SIMD and tile classes are those of
+// fa_fwd16_kernel (fa_fwd.hip), with one workgroup per row tile (the plain
+// launch order of fa_plain_tile_of); the K/V rings have four slots (8 KB
+// blocks), and the leading wavefronts load both K and V at the start of
+// their matrix phase: here the softmax phase, not the matrix phase, is the
+// longer half of a step, so its wavefronts issue no loads.
 // What differs:
 //  * S^T = K Q^T contracts 64 head-dim elements per product.  Lane (row
 //    l32, half h) of both operands holds elements 64s + 32h .. 64s + 32h + 31
@@ -176,8 +179,8 @@ __device__ __forceinline__ void store_output8(const FaFwdParams& p, const fa_f32
 
 // Eight wavefronts, 32 query rows each, two per SIMD, half a key block apart
 // (see fa_fwd16_kernel for the schedule and the ring discipline; here the
-// rings have four slots, so K(kt+3) and V(kt+3) are loaded while block kt is
-// computed).
+// rings have four slots, and K(kt+3) and V(kt+2) are loaded while block kt
+// is computed).
 template <int D, int OUT_DT>
 __global__ void __launch_bounds__(FA_WAVES_16 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd8_kernel(FaFwdParams p) {
@@ -365,19 +368,23 @@ fa_fwd8_kernel(FaFwdParams p) {
     l_lane += psum;
   };
 
+  // The leading wavefronts load both matrices, at the start of their matrix
+  // phase: K(kt+3) into K(kt-1)'s slot and V(kt+2) into V(kt-2)'s, both
+  // last read in step kt-1.  The trailing wavefronts load nothing.
   auto issue_step = [&](int kt, int s) {
-    if (kt + NSL - 1 < kv_hi) {
-      if (lead)
-        issue(Kh, koff, kbuf((s + NSL - 1) % NSL), kt + NSL - 1);
-      else
-        issue(Vh, voff, vbuf((s + NSL - 1) % NSL), kt + NSL - 1);
-    }
+    if (kt + NSL - 1 < kv_hi) issue(Kh, koff, kbuf((s + NSL - 1) % NSL), kt + NSL - 1);
+    if (kt + NSL - 2 < kv_hi) issue(Vh, voff, vbuf((s + NSL - 2) % NSL), kt + NSL - 2);
   };
-  // block kt+1 must have landed; blocks kt+2 and kt+3 may stay in flight
+  // At the end of a leading wavefront's softmax phase K(kt+1) and V(kt) must
+  // have landed (issued in step kt-2, before every later load); the loads of
+  // steps kt-1 (K(kt+2), V(kt+1)) and kt (K(kt+3), V(kt+2)) may stay in
+  // flight.
   auto wait_step = [&](int kt) {
     if (kt + 3 < kv_hi)
-      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(2 * LPW));
+      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(4 * LPW));
     else if (kt + 2 < kv_hi)
+      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(3 * LPW));
+    else if (kt + 1 < kv_hi)
       __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(LPW));
     else
       __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
@@ -390,12 +397,12 @@ fa_fwd8_kernel(FaFwdParams p) {
         p.tiles[((size_t)bh * n_row_blocks + qb0 / FA_ROW_BLOCK) * n_key_blocks + kt] =
             (unsigned char)(cls_cur + 1);
     }
+    if (lead) issue_step(kt, s);
     phase_mfma(s, (s + NSL - 1) % NSL);
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
     barrier_nofence();
     phase_softmax(kt, cls_cur);
-    issue_step(kt, s);
-    wait_step(kt);
+    if (lead) wait_step(kt);
     __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
     barrier_nofence();
   };
@@ -406,10 +413,8 @@ fa_fwd8_kernel(FaFwdParams p) {
     issue(Kh, koff, kbuf(0), kv_lo);
     if (kv_lo + 1 < kv_hi) issue(Kh, koff, kbuf(1), kv_lo + 1);
     if (kv_lo + 2 < kv_hi) issue(Kh, koff, kbuf(2), kv_lo + 2);
-  } else {
     issue(Vh, voff, vbuf(0), kv_lo);
     if (kv_lo + 1 < kv_hi) issue(Vh, voff, vbuf(1), kv_lo + 1);
-    if (kv_lo + 2 < kv_hi) issue(Vh, voff, vbuf(2), kv_lo + 2);
   }
   static_assert(TILEB % (NW * 64 * 16) == 0, "zero fill must cover the slot");
 #pragma unroll

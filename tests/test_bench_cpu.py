@@ -73,12 +73,17 @@ def test_kernel_fingerprint_follows_code_not_comments(tmp_path, monkeypatch):
         p.write_text(open(os.path.join(ROOT, r), encoding="utf-8").read(), encoding="utf-8")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     h0 = bench.kernel_source_hash()
+    h16, h8 = bench.kernel_source_hash(si.HEADLINE), bench.kernel_source_hash(si.FP8_WORKLOADS[0])
+    assert len({h0, h16, h8}) == 3
     (tmp_path / rel).write_text("// a new comment line\n" + src.replace("\n", "\n\n", 3),
                                 encoding="utf-8")
     assert bench.kernel_source_hash() == h0
     (tmp_path / rel).write_text(src.replace("#define FA_OPND_AHEAD 6", "#define FA_OPND_AHEAD 4"),
                                 encoding="utf-8")
     assert bench.kernel_source_hash() != h0
+    # a change to the 16-bit kernel voids its workloads' records, not the 8-bit one's
+    assert bench.kernel_source_hash(si.HEADLINE) != h16
+    assert bench.kernel_source_hash(si.FP8_WORKLOADS[0]) == h8
 
 
 def test_traffic_record_is_used_only_for_the_current_kernel(tmp_path, monkeypatch):
@@ -86,12 +91,12 @@ def test_traffic_record_is_used_only_for_the_current_kernel(tmp_path, monkeypatc
     f = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
     assert bench.load_traffic(w) is None  # no record
-    rec = {"kernel_src_sha256": bench.kernel_source_hash(),
-           "workloads": {w.name: {"hbm_bytes_per_launch": 123456789}}}
+    rec = {"workloads": {w.name: {"kernel_src_sha256": bench.kernel_source_hash(w),
+                                  "hbm_bytes_per_launch": 123456789}}}
     f.write_text(json.dumps(rec))
     assert bench.load_traffic(w) == 123456789
     assert bench.load_traffic(si.WORKLOADS[0]) is None  # another workload
-    rec["kernel_src_sha256"] = "0" * 64
+    rec["workloads"][w.name]["kernel_src_sha256"] = bench.kernel_source_hash(si.FP8_WORKLOADS[0])
     f.write_text(json.dumps(rec))
     assert bench.load_traffic(w) is None  # counters of another kernel
 
