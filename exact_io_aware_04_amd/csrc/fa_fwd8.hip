@@ -11,10 +11,10 @@
 // v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32), twice the rate of the
 // 16-bit products.
 //
-// Ping-pong of the two wavefronts of a SIMD and tile classes are those of
-// fa_fwd16_kernel (fa_fwd.hip), with one workgroup per row tile (the plain
-// launch order of fa_plain_tile_of); the K/V rings have four slots (8 KB
-// blocks), and the leading wavefronts load both K and V at the start of
+// Ping-pong of the two wavefronts of a SIMD, tile classes and the
+// persistent work order are those of fa_fwd16_kernel (fa_fwd.hip), without
+// its K/V stream across tiles (each tile starts its own); the K/V rings have
+// four slots (8 KB blocks), and the leading wavefronts load both K and V at the start of
 // their matrix phase: here the softmax phase, not the matrix phase, is the
 // longer half of a step, so its wavefronts issue no loads.
 // What differs:
@@ -212,229 +212,236 @@ fa_fwd8_kernel(FaFwdParams p) {
   const int half = lane >> 5;
   const int N = p.N;
 
+  // Persistent: this workgroup's row tiles in the order of fa_persist_tile_of
+  // (one workgroup per compute unit; under a causal mask or none, the tiles
+  // an XCD runs together read one key/value head, so its L2 serves their
+  // common key and value blocks).
   int bh, q0;
-  work_item<ROWS_WG>(p, bh, q0);
-  const int q1 = min(q0 + ROWS_WG, N);
-  const int qb0 = q0 + wave * FA_ROW_BLOCK;
-  const int qb1 = min(qb0 + FA_ROW_BLOCK, N);
-  const int qi = qb0 + l32;
+  for (int tile_k = 0; persist_tile(p, tile_k, bh, q0, ROWS_WG); ++tile_k) {
+    const int q1 = min(q0 + ROWS_WG, N);
+    const int qb0 = q0 + wave * FA_ROW_BLOCK;
+    const int qb1 = min(qb0 + FA_ROW_BLOCK, N);
+    const int qi = qb0 + l32;
 
-  const size_t head_bytes = (size_t)N * ROWB;
-  const size_t kv_bytes = (size_t)(bh / p.kv_group) * head_bytes;
-  const unsigned char* Qh = (const unsigned char*)p.q + (size_t)bh * head_bytes;
-  const unsigned char* Kh = (const unsigned char*)p.k + kv_bytes;
-  const unsigned char* Vh = (const unsigned char*)p.v + kv_bytes;
+    const size_t head_bytes = (size_t)N * ROWB;
+    const size_t kv_bytes = (size_t)(bh / p.kv_group) * head_bytes;
+    const unsigned char* Qh = (const unsigned char*)p.q + (size_t)bh * head_bytes;
+    const unsigned char* Kh = (const unsigned char*)p.k + kv_bytes;
+    const unsigned char* Vh = (const unsigned char*)p.v + kv_bytes;
 
-  int kv_lo, kv_hi;
-  fa_key_block_range(q0, q1, BC, N, p.mask_kind, p.window, &kv_lo, &kv_hi);
+    int kv_lo, kv_hi;
+    fa_key_block_range(q0, q1, BC, N, p.mask_kind, p.window, &kv_lo, &kv_hi);
 
-  // Q fragment s holds q[qi][64s + 32half .. +31]; rows past N read row N-1
-  // (no branch) and are never stored.
-  fa_u32x8 qf[NS];
-  {
-    const unsigned char* qrow = Qh + (size_t)min(qi, N - 1) * ROWB;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const fa_u32x4 lo = *(const fa_u32x4*)(qrow + 64 * s + 32 * half);
-      const fa_u32x4 hi = *(const fa_u32x4*)(qrow + 64 * s + 32 * half + 16);
-      qf[s] = fa_u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    // Q fragment s holds q[qi][64s + 32half .. +31]; rows past N read row N-1
+    // (no branch) and are never stored.
+    fa_u32x8 qf[NS];
+    {
+      const unsigned char* qrow = Qh + (size_t)min(qi, N - 1) * ROWB;
+  #pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const fa_u32x4 lo = *(const fa_u32x4*)(qrow + 64 * s + 32 * half);
+        const fa_u32x4 hi = *(const fa_u32x4*)(qrow + 64 * s + 32 * half + 16);
+        qf[s] = fa_u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
     }
-  }
 
-  // Global byte offset (within a block) of this lane's 16 bytes in a loading
-  // wave's first one-kilobyte LDS piece (8 rows), swizzle applied; piece i
-  // lies 4 KB (32 rows) further on both sides.
-  unsigned koff, voff;
-  {
-    const int o = (wave % NL) * 1024 + 16 * lane;
-    const int r = o / ROWB, pos = (o % ROWB) / 16;
-    koff = r * ROWB + 16 * (pos ^ kswz8(r));
-    voff = r * ROWB + 16 * (pos ^ vswz8(r));
-  }
-  // LDS read offsets.  K slice s, piece e: row l32, chunk 4s + 2half + e.
-  // V^T for output block cb: lane 16g + a addresses row 8(a/8) + 4half +
-  // (a/2)%4 (+16i for read i), columns 32cb + 16(g%2) + 8(a%2) .. +7.
-  unsigned kread[NS][2], vread[NCB];
-#pragma unroll
-  for (int s = 0; s < NS; ++s)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) kread[s][e] = l32 * ROWB + 16 * ((4 * s + 2 * half + e) ^ kswz8(l32));
-  {
-    const int g = lane >> 4, a = lane & 15;
-    const int vr = 8 * (a >> 3) + 4 * half + ((a >> 1) & 3);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-      vread[cb] = vr * ROWB + 16 * ((2 * cb + (g & 1)) ^ vswz8(vr)) + 8 * (a & 1);
-  }
-
-  // K or V block kt -> LDS slot (descriptor ends at key N: rows past it read
-  // as zeros).
-  auto issue = [&](const unsigned char* base, unsigned off, FA_AS3 unsigned char* dst, int kt) {
-    const int k0 = kt * BC;
-    const int nb = (min(N - k0, BC)) * ROWB;
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * ROWB), 0, nb, FA_BUF_WORD3);
-#pragma unroll
-    for (int i = 0; i < LPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (FA_AS3 void*)(dst + (i * NL + wave % NL) * 1024), 16, (int)off, i * NL * 1024, 0, 0);
-  };
-
-  fa_f32x16 acc[NCB];  // O^T: acc[cb] holds columns 32cb.., row qi
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-  // reference m (base 2) and this lane's sum of the unrounded scaled
-  // probabilities 2^(s c2 - m + 3)
-  float m_ref = FA_NEG_INF, l_lane = 0.f;
-  const float c2 = p.scale_log2;
-  const float inv_c2 = 1.f / p.scale_log2;
-  const int n_row_blocks = (N + FA_ROW_BLOCK - 1) / FA_ROW_BLOCK;
-  const int n_key_blocks = (N + BC - 1) / BC;
-
-  // Scores of the current block (matrix phase -> softmax phase) and its
-  // rounded probabilities (softmax phase -> the next matrix phase).
-  // sc[kb][r] is key k0 + 32kb + 8(r/4) + 4half + r%4 of row qi.  The score
-  // accumulators start from -(m - 3) / c2 (0 while the row has seen no key),
-  // so the matrix core delivers (s c2 - m + 3) / c2.
-  fa_f32x16 sc[NKB];
-  fa_u32x8 pf = fa_u32x8{0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  fa_f32x16 sc0;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) sc0[r] = 0.f;
-
-  auto phase_mfma = [&](int ks, int vs) {
-    matrix_phase8<D>(acc, sc, sc0, pf, qf, kbuf(ks), vbuf(vs), kread, vread);
-  };
-  // Softmax phase of block kt.  Fast path (fully visible block, row already
-  // started): p = 2^t straight from the scores, accepted if the lane's sum
-  // is at most 2^8 (so is each p).  Exact path: mask, row maximum, new
-  // reference, rescale of O and the sum, probabilities again (each then at
-  // most 2^3, their sum at most 2^8).
-  auto phase_softmax = [&](int kt, int cls) {
-    if (cls == FA_TILE_SKIP) {
-      pf = fa_u32x8{0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-      return;
+    // Global byte offset (within a block) of this lane's 16 bytes in a loading
+    // wave's first one-kilobyte LDS piece (8 rows), swizzle applied; piece i
+    // lies 4 KB (32 rows) further on both sides.
+    unsigned koff, voff;
+    {
+      const int o = (wave % NL) * 1024 + 16 * lane;
+      const int r = o / ROWB, pos = (o % ROWB) / 16;
+      koff = r * ROWB + 16 * (pos ^ kswz8(r));
+      voff = r * ROWB + 16 * (pos ^ vswz8(r));
     }
-    float pr[NKB][16];
-    float psum = 0.f;
-    float ps4[4];  // four independent partial sums (short dependency chains)
-    bool exact = cls == FA_TILE_PARTIAL || __ballot(m_ref == FA_NEG_INF);
-    if (!exact) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pr[kb][r] = exp2_hw(sc[kb][r] * c2);
-          ps4[r & 3] = kb == 0 && r < 4 ? pr[kb][r] : ps4[r & 3] + pr[kb][r];
-        }
-      psum = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
-      exact = __ballot(!(psum <= 256.f));
-    }
-    if (exact) {
-      if (cls == FA_TILE_PARTIAL) apply_mask<NKB>(sc, kt * BC, qi, half, N, p.mask_kind, p.window);
-      // the accumulators hold (s c2 - base) / c2
-      const float base = m_ref == FA_NEG_INF ? 0.f : m_ref - FA8_SHIFT;
-      float mx = FA_NEG_INF;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      mx = pair_max(mx) * c2;  // block maximum of s c2 - base (-inf: nothing visible)
-      const float m_new = fmaxf(m_ref, mx == FA_NEG_INF ? FA_NEG_INF : base + mx);
-      const float alpha = m_new > m_ref ? (m_ref == FA_NEG_INF ? 0.f : exp2_hw(m_ref - m_new)) : 1.f;
-      m_ref = m_new;
-      l_lane *= alpha;
-#pragma unroll
+    // LDS read offsets.  K slice s, piece e: row l32, chunk 4s + 2half + e.
+    // V^T for output block cb: lane 16g + a addresses row 8(a/8) + 4half +
+    // (a/2)%4 (+16i for read i), columns 32cb + 16(g%2) + 8(a%2) .. +7.
+    unsigned kread[NS][2], vread[NCB];
+  #pragma unroll
+    for (int s = 0; s < NS; ++s)
+  #pragma unroll
+      for (int e = 0; e < 2; ++e) kread[s][e] = l32 * ROWB + 16 * ((4 * s + 2 * half + e) ^ kswz8(l32));
+    {
+      const int g = lane >> 4, a = lane & 15;
+      const int vr = 8 * (a >> 3) + 4 * half + ((a >> 1) & 3);
+  #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
-      const float shift = m_ref == FA_NEG_INF ? 0.f : base - m_ref + FA8_SHIFT;
-      psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pr[kb][r] = exp2_hw(__builtin_fmaf(sc[kb][r], c2, shift));
-          ps4[r & 3] = kb == 0 && r < 4 ? pr[kb][r] : ps4[r & 3] + pr[kb][r];
-        }
-      psum = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
-      const float mn = m_ref == FA_NEG_INF ? 0.f : -(m_ref - FA8_SHIFT) * inv_c2;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc0[r] = mn;
+        vread[cb] = vr * ROWB + 16 * ((2 * cb + (g & 1)) ^ vswz8(vr)) + 8 * (a & 1);
     }
-    pf = pack_e4m3(pr);
-    l_lane += psum;
-  };
 
-  // The leading wavefronts load both matrices, at the start of their matrix
-  // phase: K(kt+3) into K(kt-1)'s slot and V(kt+2) into V(kt-2)'s, both
-  // last read in step kt-1.  The trailing wavefronts load nothing.
-  auto issue_step = [&](int kt, int s) {
-    if (kt + NSL - 1 < kv_hi) issue(Kh, koff, kbuf((s + NSL - 1) % NSL), kt + NSL - 1);
-    if (kt + NSL - 2 < kv_hi) issue(Vh, voff, vbuf((s + NSL - 2) % NSL), kt + NSL - 2);
-  };
-  // At the end of a leading wavefront's softmax phase K(kt+1) and V(kt) must
-  // have landed (issued in step kt-2, before every later load); the loads of
-  // steps kt-1 (K(kt+2), V(kt+1)) and kt (K(kt+3), V(kt+2)) may stay in
-  // flight.
-  auto wait_step = [&](int kt) {
-    if (kt + 3 < kv_hi)
-      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(4 * LPW));
-    else if (kt + 2 < kv_hi)
-      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(3 * LPW));
-    else if (kt + 1 < kv_hi)
-      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(LPW));
-    else
-      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
-  };
-  auto step = [&](int kt, int s) {
-    int cls_cur = FA_TILE_SKIP;
-    if (kt < kv_hi) {
-      cls_cur = fa_classify(qb0, qb1, kt * BC, BC, N, p.mask_kind, p.window);
-      if (p.tiles && lane == 0 && qb0 < N)
-        p.tiles[((size_t)bh * n_row_blocks + qb0 / FA_ROW_BLOCK) * n_key_blocks + kt] =
-            (unsigned char)(cls_cur + 1);
+    // K or V block kt -> LDS slot (descriptor ends at key N: rows past it read
+    // as zeros).
+    auto issue = [&](const unsigned char* base, unsigned off, FA_AS3 unsigned char* dst, int kt) {
+      const int k0 = kt * BC;
+      const int nb = (min(N - k0, BC)) * ROWB;
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * ROWB), 0, nb, FA_BUF_WORD3);
+  #pragma unroll
+      for (int i = 0; i < LPW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (FA_AS3 void*)(dst + (i * NL + wave % NL) * 1024), 16, (int)off, i * NL * 1024, 0, 0);
+    };
+
+    fa_f32x16 acc[NCB];  // O^T: acc[cb] holds columns 32cb.., row qi
+  #pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+    // reference m (base 2) and this lane's sum of the unrounded scaled
+    // probabilities 2^(s c2 - m + 3)
+    float m_ref = FA_NEG_INF, l_lane = 0.f;
+    const float c2 = p.scale_log2;
+    const float inv_c2 = 1.f / p.scale_log2;
+    const int n_row_blocks = (N + FA_ROW_BLOCK - 1) / FA_ROW_BLOCK;
+    const int n_key_blocks = (N + BC - 1) / BC;
+
+    // Scores of the current block (matrix phase -> softmax phase) and its
+    // rounded probabilities (softmax phase -> the next matrix phase).
+    // sc[kb][r] is key k0 + 32kb + 8(r/4) + 4half + r%4 of row qi.  The score
+    // accumulators start from -(m - 3) / c2 (0 while the row has seen no key),
+    // so the matrix core delivers (s c2 - m + 3) / c2.
+    fa_f32x16 sc[NKB];
+    fa_u32x8 pf = fa_u32x8{0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    fa_f32x16 sc0;
+  #pragma unroll
+    for (int r = 0; r < 16; ++r) sc0[r] = 0.f;
+
+    auto phase_mfma = [&](int ks, int vs) {
+      matrix_phase8<D>(acc, sc, sc0, pf, qf, kbuf(ks), vbuf(vs), kread, vread);
+    };
+    // Softmax phase of block kt.  Fast path (fully visible block, row already
+    // started): p = 2^t straight from the scores, accepted if the lane's sum
+    // is at most 2^8 (so is each p).  Exact path: mask, row maximum, new
+    // reference, rescale of O and the sum, probabilities again (each then at
+    // most 2^3, their sum at most 2^8).
+    auto phase_softmax = [&](int kt, int cls) {
+      if (cls == FA_TILE_SKIP) {
+        pf = fa_u32x8{0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        return;
+      }
+      float pr[NKB][16];
+      float psum = 0.f;
+      float ps4[4];  // four independent partial sums (short dependency chains)
+      bool exact = cls == FA_TILE_PARTIAL || __ballot(m_ref == FA_NEG_INF);
+      if (!exact) {
+  #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            pr[kb][r] = exp2_hw(sc[kb][r] * c2);
+            ps4[r & 3] = kb == 0 && r < 4 ? pr[kb][r] : ps4[r & 3] + pr[kb][r];
+          }
+        psum = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+        exact = __ballot(!(psum <= 256.f));
+      }
+      if (exact) {
+        if (cls == FA_TILE_PARTIAL) apply_mask<NKB>(sc, kt * BC, qi, half, N, p.mask_kind, p.window);
+        // the accumulators hold (s c2 - base) / c2
+        const float base = m_ref == FA_NEG_INF ? 0.f : m_ref - FA8_SHIFT;
+        float mx = FA_NEG_INF;
+  #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+        mx = pair_max(mx) * c2;  // block maximum of s c2 - base (-inf: nothing visible)
+        const float m_new = fmaxf(m_ref, mx == FA_NEG_INF ? FA_NEG_INF : base + mx);
+        const float alpha = m_new > m_ref ? (m_ref == FA_NEG_INF ? 0.f : exp2_hw(m_ref - m_new)) : 1.f;
+        m_ref = m_new;
+        l_lane *= alpha;
+  #pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+        const float shift = m_ref == FA_NEG_INF ? 0.f : base - m_ref + FA8_SHIFT;
+        psum = 0.f;
+  #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            pr[kb][r] = exp2_hw(__builtin_fmaf(sc[kb][r], c2, shift));
+            ps4[r & 3] = kb == 0 && r < 4 ? pr[kb][r] : ps4[r & 3] + pr[kb][r];
+          }
+        psum = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+        const float mn = m_ref == FA_NEG_INF ? 0.f : -(m_ref - FA8_SHIFT) * inv_c2;
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) sc0[r] = mn;
+      }
+      pf = pack_e4m3(pr);
+      l_lane += psum;
+    };
+
+    // The leading wavefronts load both matrices, at the start of their matrix
+    // phase: K(kt+3) into K(kt-1)'s slot and V(kt+2) into V(kt-2)'s, both
+    // last read in step kt-1.  The trailing wavefronts load nothing.
+    auto issue_step = [&](int kt, int s) {
+      if (kt + NSL - 1 < kv_hi) issue(Kh, koff, kbuf((s + NSL - 1) % NSL), kt + NSL - 1);
+      if (kt + NSL - 2 < kv_hi) issue(Vh, voff, vbuf((s + NSL - 2) % NSL), kt + NSL - 2);
+    };
+    // At the end of a leading wavefront's softmax phase K(kt+1) and V(kt) must
+    // have landed (issued in step kt-2, before every later load); the loads of
+    // steps kt-1 (K(kt+2), V(kt+1)) and kt (K(kt+3), V(kt+2)) may stay in
+    // flight.
+    auto wait_step = [&](int kt) {
+      if (kt + 3 < kv_hi)
+        __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(4 * LPW));
+      else if (kt + 2 < kv_hi)
+        __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(3 * LPW));
+      else if (kt + 1 < kv_hi)
+        __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(LPW));
+      else
+        __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
+    };
+    auto step = [&](int kt, int s) {
+      int cls_cur = FA_TILE_SKIP;
+      if (kt < kv_hi) {
+        cls_cur = fa_classify(qb0, qb1, kt * BC, BC, N, p.mask_kind, p.window);
+        if (p.tiles && lane == 0 && qb0 < N)
+          p.tiles[((size_t)bh * n_row_blocks + qb0 / FA_ROW_BLOCK) * n_key_blocks + kt] =
+              (unsigned char)(cls_cur + 1);
+      }
+      if (lead) issue_step(kt, s);
+      phase_mfma(s, (s + NSL - 1) % NSL);
+      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
+      barrier_nofence();
+      phase_softmax(kt, cls_cur);
+      if (lead) wait_step(kt);
+      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
+      barrier_nofence();
+    };
+
+    // Prologue: K and V of the first two blocks, and zeros in the V slot that
+    // the first step's (probability 0) P V product reads.
+    if (lead) {
+      issue(Kh, koff, kbuf(0), kv_lo);
+      if (kv_lo + 1 < kv_hi) issue(Kh, koff, kbuf(1), kv_lo + 1);
+      if (kv_lo + 2 < kv_hi) issue(Kh, koff, kbuf(2), kv_lo + 2);
+      issue(Vh, voff, vbuf(0), kv_lo);
+      if (kv_lo + 1 < kv_hi) issue(Vh, voff, vbuf(1), kv_lo + 1);
     }
-    if (lead) issue_step(kt, s);
-    phase_mfma(s, (s + NSL - 1) % NSL);
-    __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
-    barrier_nofence();
-    phase_softmax(kt, cls_cur);
-    if (lead) wait_step(kt);
-    __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
-    barrier_nofence();
-  };
-
-  // Prologue: K and V of the first two blocks, and zeros in the V slot that
-  // the first step's (probability 0) P V product reads.
-  if (lead) {
-    issue(Kh, koff, kbuf(0), kv_lo);
-    if (kv_lo + 1 < kv_hi) issue(Kh, koff, kbuf(1), kv_lo + 1);
-    if (kv_lo + 2 < kv_hi) issue(Kh, koff, kbuf(2), kv_lo + 2);
-    issue(Vh, voff, vbuf(0), kv_lo);
-    if (kv_lo + 1 < kv_hi) issue(Vh, voff, vbuf(1), kv_lo + 1);
+    static_assert(TILEB % (NW * 64 * 16) == 0, "zero fill must cover the slot");
+  #pragma unroll
+    for (int i = 0; i < TILEB / (NW * 64 * 16); ++i)
+      *(FA_AS3 fa_u32x4*)(vbuf(NSL - 1) + (i * NW * 64 + tid) * 16) = fa_u32x4{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (!lead) barrier_nofence();
+    for (int kt = kv_lo;;) {
+      step(kt, 0);
+      if (++kt > kv_hi) break;
+      step(kt, 1);
+      if (++kt > kv_hi) break;
+      step(kt, 2);
+      if (++kt > kv_hi) break;
+      step(kt, 3);
+      if (++kt > kv_hi) break;
+    }
+    if (lead) barrier_nofence();
+    store_output8<D, OUT_DT>(p, acc, m_ref, pair_sum(l_lane), bh, qi, half);
+    // every wavefront is done with the slots before the next tile refills them
+    __syncthreads();
   }
-  static_assert(TILEB % (NW * 64 * 16) == 0, "zero fill must cover the slot");
-#pragma unroll
-  for (int i = 0; i < TILEB / (NW * 64 * 16); ++i)
-    *(FA_AS3 fa_u32x4*)(vbuf(NSL - 1) + (i * NW * 64 + tid) * 16) = fa_u32x4{0u, 0u, 0u, 0u};
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (!lead) barrier_nofence();
-  for (int kt = kv_lo;;) {
-    step(kt, 0);
-    if (++kt > kv_hi) break;
-    step(kt, 1);
-    if (++kt > kv_hi) break;
-    step(kt, 2);
-    if (++kt > kv_hi) break;
-    step(kt, 3);
-    if (++kt > kv_hi) break;
-  }
-  if (lead) barrier_nofence();
-  store_output8<D, OUT_DT>(p, acc, m_ref, pair_sum(l_lane), bh, qi, half);
 }
 
 // One wavefront, one E4M3 product (lane-order operands of 32 bytes in,
@@ -463,7 +470,7 @@ __global__ void __launch_bounds__(64) fa_probe8_kernel(const void* a, const void
 
 template <int D, int OUT_DT>
 hipError_t launch8(const FaFwdParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.BH * p.n_row_tiles));
+  const dim3 grid((unsigned)(p.n_groups * p.wg_per_group));
   hipLaunchKernelGGL((fa_fwd8_kernel<D, OUT_DT>), grid, dim3(FA_WAVES_16 * 64), 0, stream, p);
   return hipGetLastError();
 }

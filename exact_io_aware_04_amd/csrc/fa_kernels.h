@@ -126,11 +126,11 @@ constexpr int fa_rows_per_wg(int in_dtype, int d) {
   return (in_dtype == 0 ? FA_WAVES_32 : d == 256 ? FA_WAVES_WIDE : FA_WAVES_16) * FA_ROW_BLOCK;
 }
 
-// The forward launch with one persistent workgroup per compute unit: the
-// f16/bf16 kernel at d = 64 and 128.  Every other forward kernel is launched
-// with one workgroup per row tile.
+// The forward launches with one persistent workgroup per compute unit: the
+// f16/bf16 kernel at d = 64 and 128 and the E4M3 kernel (d = 128).  The
+// fp32 and d = 256 kernels are launched with one workgroup per row tile.
 constexpr bool fa_fwd_persistent(int in_dtype, int d) {
-  return (in_dtype == 1 || in_dtype == 2) && d <= 128;
+  return (in_dtype == 1 || in_dtype == 2 || in_dtype == FA_DT_E4M3) && d <= 128;
 }
 
 // Work order of the forward, shared by the host (launch plan, schedule

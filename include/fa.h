@@ -302,7 +302,7 @@ int fa_tile_map(int N, int d, int in_dtype, int mask_kind, int window,
  * rows_per_workgroup query rows (fa_tile_shape) of one (batch, head) slice.
  * *n_workgroups receives the grid size G and *max_tiles the largest number
  * R of tiles any workgroup takes (R = 1 where each workgroup takes one
- * tile: f32 inputs, d = 256, E4M3).  With `out` non-null (host memory of
+ * tile: f32 inputs, d = 256).  With `out` non-null (host memory of
  * out_len >= 2*G*R ints) out[2(g*R + k)] and out[2(g*R + k) + 1] receive the
  * batch*head index and the row tile index of workgroup g's k-th tile, or
  * -1 and -1 after its last one.  Every row tile appears exactly once.  The

@@ -57,7 +57,7 @@ def key_blocks(qt, rows, N, mask, window, bc=64):
 
 
 def persistent(dtype, d):
-    return dtype in (F16, BF16) and d <= 128
+    return dtype in (F16, BF16, E4M3) and d <= 128
 
 
 @pytest.mark.parametrize("case", ALL, ids=case_id)
