@@ -61,7 +61,7 @@ enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_SLIDING = 2 };
 enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad enum, misalignment */
-  FA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement   */
+  FA_ERR_UNSUPPORTED = 2, /* valid request the library does not implement  */
   FA_ERR_NO_DEVICE = 3,   /* no usable gfx950 device                        */
   FA_ERR_HIP = 4          /* the HIP runtime reported an error              */
 };
