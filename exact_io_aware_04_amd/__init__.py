@@ -76,7 +76,7 @@ def load():
     lib.fa_tile_shape.restype = i
     lib.fa_tile_map.argtypes = [i, i, i, i, i, vp]
     lib.fa_tile_map.restype = i
-    lib.fa_fwd_schedule.argtypes = [i, i, i, i, i, i, i, i, ip, ip, vp, ctypes.c_longlong]
+    lib.fa_fwd_schedule.argtypes = [i, i, i, i, i, i, i, i, i, ip, ip, vp, ctypes.c_longlong]
     lib.fa_fwd_schedule.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -181,19 +181,19 @@ def fa_tile_map(N: int, d: int, in_dtype: int, mask_kind: int, window: int):
 
 
 def fa_fwd_schedule(B: int, H: int, N: int, d: int, in_dtype: int, mask_kind: int,
-                    compute_units: int, H_kv: int = None):
+                    compute_units: int, H_kv: int = None, window: int = 0):
     """Forward work order: a list with one entry per workgroup, each the
     list of (batch*head, row tile) pairs it takes, in order."""
     G, R = ctypes.c_int(0), ctypes.c_int(0)
     lib = load()
     H_kv = H if H_kv is None else H_kv
-    st = lib.fa_fwd_schedule(B, H, H_kv, N, d, in_dtype, mask_kind, compute_units,
+    st = lib.fa_fwd_schedule(B, H, H_kv, N, d, in_dtype, mask_kind, window, compute_units,
                              ctypes.byref(G), ctypes.byref(R), None, 0)
     if st != FA_OK:
         raise FaError(st, "fa_fwd_schedule")
     n = 2 * G.value * R.value
     buf = (ctypes.c_int * n)()
-    st = lib.fa_fwd_schedule(B, H, H_kv, N, d, in_dtype, mask_kind, compute_units,
+    st = lib.fa_fwd_schedule(B, H, H_kv, N, d, in_dtype, mask_kind, window, compute_units,
                              ctypes.byref(G), ctypes.byref(R), ctypes.cast(buf, ctypes.c_void_p), n)
     if st != FA_OK:
         raise FaError(st, "fa_fwd_schedule")

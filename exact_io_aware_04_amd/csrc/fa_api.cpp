@@ -166,7 +166,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   if (!(p.scale_log2 >= FLT_MIN)) p.scale_log2 = FLT_MIN;
   p.v_scale = v_scale;
   p.n_row_tiles = (N + fa_rows_per_wg(in_dtype, d) - 1) / fa_rows_per_wg(in_dtype, d);
-  fa_fwd_plan(p, mask_kind, device_cus());
+  fa_fwd_plan(p, mask_kind, device_cus(), fa_rows_per_wg(in_dtype, d));
   hipError_t e = in_dtype == FA_DTYPE_E4M3
                      ? fa_launch_fwd8(out_dtype, d, p, (hipStream_t)stream)
                      : fa_launch_fwd(in_dtype, out_dtype, d, p, (hipStream_t)stream);
@@ -556,7 +556,7 @@ int fa_tile_map(int N, int d, int in_dtype, int mask_kind, int window, unsigned 
 }
 
 int fa_fwd_schedule(int B, int H, int H_kv, int N, int d, int in_dtype, int mask_kind,
-                    int compute_units, int* n_workgroups, int* max_tiles, int* out,
+                    int window, int compute_units, int* n_workgroups, int* max_tiles, int* out,
                     long long out_len) {
   if (!n_workgroups || !max_tiles) return fail(FA_ERR_INVALID_ARG, "null output pointer");
   if (B < 1 || H < 1 || N < 1 || N >= (1 << 30) || compute_units < 1)
@@ -568,6 +568,8 @@ int fa_fwd_schedule(int B, int H, int H_kv, int N, int d, int in_dtype, int mask
     return fail(FA_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
   if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL && mask_kind != FA_MASK_SLIDING)
     return fail(FA_ERR_INVALID_ARG, "unknown mask_kind %d", mask_kind);
+  if (mask_kind == FA_MASK_SLIDING && window < 1)
+    return fail(FA_ERR_INVALID_ARG, "sliding window must be >= 1 (got %d)", window);
   if (!fa_head_dim_built(in_dtype, d))
     return fail(FA_ERR_UNSUPPORTED, "head dim %d not built for in_dtype %d", d, in_dtype);
   const int rows = fa_rows_per_wg(in_dtype, d);
@@ -577,8 +579,10 @@ int fa_fwd_schedule(int B, int H, int H_kv, int N, int d, int in_dtype, int mask
   FaFwdParams p{};
   p.BH = B * H;
   p.kv_group = H / H_kv;
+  p.N = N;
+  p.window = mask_kind == FA_MASK_SLIDING ? (window < N ? window : N) : 0;
   p.n_row_tiles = (int)T;
-  fa_fwd_plan(p, mask_kind, compute_units);
+  fa_fwd_plan(p, mask_kind, compute_units, rows);
   const bool persistent = fa_fwd_persistent(in_dtype, d);
   const long long G = persistent ? (long long)p.n_groups * p.wg_per_group : (long long)p.BH * T;
   const long long R = persistent ? (p.tiles_per_group + p.wg_per_group - 1) / p.wg_per_group : 1;

@@ -32,9 +32,12 @@ struct FaFwdParams {
   int n_groups;
   int wg_per_group;
   int tiles_per_group;
-  int kv_major;           // 1: a group's row tiles numbered K/V head by K/V head
+  int kv_major;           // numbering of a group's row tiles: 0 heads fastest,
+                          // 1 K/V head by K/V head, 2 window teams
   int kv_share;           // query heads of one K/V head within a group (numbered
-                          // fastest under kv_major)
+                          // fastest under kv_major = 1)
+  int team;               // kv_major = 2: workgroups per team (window / rows per
+                          // workgroup)
 };
 
 // Backward pass (fa_bwd.hip).
@@ -174,14 +177,40 @@ FA_HD void fa_plain_tile_of(const FaFwdParams& p, int b, int* bh, int* qt) {
 //     every pair of snake rounds pairs position t with 2J-1-t at equal
 //     summed length: no mask, or causal with G T a multiple or divisor of
 //     2J.  (G = heads per group gives the kv_major = 0 order.)
+//   kv_major = 2 (sliding window of S row tiles exactly, S = team): no
+//     snake.  The group's J workgroups form J / S teams of S; team t takes
+//     heads t, t + J/S, ... in turn, and member i of a team takes the row
+//     tiles of a head with rank = i mod S, one after the other.  With D =
+//     row tile / key block, a tile of rank r >= S reads key blocks
+//     (r - S) D .. (r + 1) D - 1 and a tile of rank r < S blocks
+//     0 .. (r + 1) D - 1.  On even heads of the team member i takes ranks
+//     i, i + S, i + 2S, ...: its first tile ends after (i + 1) D blocks,
+//     when its next one (from block i D on) reads the block every other
+//     member reads at that moment, so the whole team streams the same
+//     key/value block at the same time from then on and the L2 serves it
+//     from one fetch.  On odd heads member i takes ranks i + S, i + 2S, ...
+//     and last rank S - 1 - i: it starts i D blocks after member 0 and its
+//     first tile i D blocks further in (aligned again); its last tile is
+//     (S - i) D blocks long, so that every member's two heads add to the
+//     same number of blocks.  Needs an even number of heads per team and T
+//     a multiple of S.
 // Once a workgroup's s passes the end, every later one does too.
 FA_HD bool fa_persist_tile_of(const FaFwdParams& p, int g, int k, int* bh, int* qt) {
   const int x = g % p.n_groups, j = g / p.n_groups;
   const int J = p.wg_per_group;
-  const int s = (k & 1) ? (k + 1) * J - 1 - j : k * J + j;
-  if (s >= p.tiles_per_group) return false;
   const int T = p.n_row_tiles;
   const int hpg = p.BH / p.n_groups;  // heads per group
+  if (p.kv_major == 2) {
+    const int S = p.team, n_team = J / S, M = T / S;  // M: tiles per head and member
+    const int team = j / S, i = j - team * S;
+    const int hh = k / M, kk = k - hh * M;
+    if (hh >= hpg / n_team) return false;
+    *bh = x * hpg + hh * n_team + team;
+    *qt = !(hh & 1) ? i + kk * S : (kk < M - 1 ? i + (kk + 1) * S : S - 1 - i);
+    return true;
+  }
+  const int s = (k & 1) ? (k + 1) * J - 1 - j : k * J + j;
+  if (s >= p.tiles_per_group) return false;
   int head, rank;
   if (p.kv_major) {
     const int G = p.kv_share, per = G * T;
@@ -201,8 +230,9 @@ FA_HD bool fa_persist_tile_of(const FaFwdParams& p, int g, int k, int* bh, int* 
 // xcd_split, heavy_first and, for the persistent launch, one workgroup per
 // compute unit (fewer when there are fewer tiles), a multiple of the 8
 // groups when every XCD owns its own heads, and the numbering.  Requires
-// BH, kv_group and n_row_tiles.
-inline void fa_fwd_plan(FaFwdParams& p, int mask_kind, int cus) {
+// BH, kv_group, N, window (sliding) and n_row_tiles = ceil(N / rows_wg);
+// key blocks of FA_KEYS_16 (= FA_KEYS_8) keys.
+inline void fa_fwd_plan(FaFwdParams& p, int mask_kind, int cus, int rows_wg) {
   p.xcd_split = (p.BH % 8 == 0) ? 1 : 0;
   p.heavy_first = mask_kind != FA_MASKK_NONE ? 1 : 0;
   const long long total = (long long)p.BH * p.n_row_tiles;
@@ -229,6 +259,20 @@ inline void fa_fwd_plan(FaFwdParams& p, int mask_kind, int cus) {
   const long long GT = (long long)p.kv_share * p.n_row_tiles, J2 = 2LL * p.wg_per_group;
   p.kv_major = mask_kind == FA_MASKK_NONE ||
                (mask_kind == FA_MASKK_CAUSAL && (GT % J2 == 0 || J2 % GT == 0));
+  // Sliding windows of a whole number S of row tiles (and row tiles of a
+  // whole number of key blocks, N a multiple of the row tile): window teams
+  // when the workgroups split into teams of S, every team gets an even
+  // number of heads and every head S-aligned ranks (fa_persist_tile_of).
+  p.team = 0;
+  if (mask_kind == FA_MASKK_SLIDING && rows_wg % FA_KEYS_16 == 0 && p.window % rows_wg == 0 &&
+      p.N % rows_wg == 0) {
+    const int S = p.window / rows_wg, J = p.wg_per_group, hpg = p.BH / p.n_groups;
+    if (S >= 1 && J % S == 0 && hpg % (2 * (J / S)) == 0 && p.n_row_tiles % S == 0 &&
+        (long long)J * (hpg / (J / S)) * (p.n_row_tiles / S) == (long long)p.tiles_per_group) {
+      p.kv_major = 2;
+      p.team = S;
+    }
+  }
 }
 
 // head dims built for an input dtype code: 64 and 128, 256 for f16/bf16,

@@ -296,9 +296,9 @@ int fa_tile_map(int N, int d, int in_dtype, int mask_kind, int window,
 /*
  * Host-side export of the forward's work order (no device call): which row
  * tiles each workgroup of the fa_fwd / fa_fwd_gqa / fa_fwd_fp8 launch for
- * (B, H, H_kv, N, d, in_dtype, mask_kind) takes (H_kv = H for fa_fwd and
- * fa_fwd_fp8), on a device with `compute_units`
- * compute units, in the order it takes them.  A row tile is
+ * (B, H, H_kv, N, d, in_dtype, mask_kind, window) takes (H_kv = H for
+ * fa_fwd and fa_fwd_fp8; window read only for the sliding mask), on a
+ * device with `compute_units` compute units, in the order it takes them.  A row tile is
  * rows_per_workgroup query rows (fa_tile_shape) of one (batch, head) slice.
  * *n_workgroups receives the grid size G and *max_tiles the largest number
  * R of tiles any workgroup takes (R = 1 where each workgroup takes one
@@ -309,12 +309,12 @@ int fa_tile_map(int N, int d, int in_dtype, int mask_kind, int window,
  * order is a performance choice (load balance, L2 reuse of each head's
  * keys and values), never a numerical one: each tile's output depends on
  * its own rows only.  FA_ERR_INVALID_ARG for sizes < 1, N >= 2^30, H not
- * a multiple of H_kv, a bad enum, a null n_workgroups or max_tiles, or
- * out_len < 2*G*R with out non-null; FA_ERR_UNSUPPORTED for a head dim not
- * built for in_dtype.
+ * a multiple of H_kv, a bad enum, a sliding window < 1, a null
+ * n_workgroups or max_tiles, or out_len < 2*G*R with out non-null;
+ * FA_ERR_UNSUPPORTED for a head dim not built for in_dtype.
  */
 int fa_fwd_schedule(int B, int H, int H_kv, int N, int d, int in_dtype, int mask_kind,
-                    int compute_units, int* n_workgroups, int* max_tiles, int* out,
+                    int window, int compute_units, int* n_workgroups, int* max_tiles, int* out,
                     long long out_len);
 
 /* Name of a status code ("FA_OK", ...).  Static storage. */

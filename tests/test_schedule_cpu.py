@@ -1,7 +1,8 @@
 """The forward's work order (fa_fwd_schedule, host only): every row tile is
-taken exactly once, the persistent workgroups' loads are balanced, and under
+taken exactly once, the persistent workgroups' loads are balanced, under
 the head-by-head numbering the tiles a group runs together share one head's
-keys and values.
+keys and values, and under the window-team order the members of a team
+read the same key block at the same time.
 
 The order decides speed and HBM traffic only (each tile's output depends on
 its own rows), so these properties are checked here on the host; the GPU
@@ -64,7 +65,7 @@ def persistent(dtype, d):
 @pytest.mark.parametrize("cus", [256, 80])
 def test_every_row_tile_exactly_once(case, cus):
     B, H, N, d, dt, mask, window, H_kv = case
-    sched = fa.fa_fwd_schedule(B, H, N, d, dt, mask, cus, H_kv=H_kv)
+    sched = fa.fa_fwd_schedule(B, H, N, d, dt, mask, cus, H_kv=H_kv, window=window)
     rows = _rows(d, dt)
     T = -(-N // rows)
     got = sorted(t for wg in sched for t in wg)
@@ -86,7 +87,7 @@ def test_persistent_loads_balanced(case):
     every workgroup takes an even number of tiles (whole snake round
     pairs); the five-case list holds such cases for each numbering."""
     B, H, N, d, dt, mask, window, H_kv = case
-    sched = fa.fa_fwd_schedule(B, H, N, d, dt, mask, 256, H_kv=H_kv)
+    sched = fa.fa_fwd_schedule(B, H, N, d, dt, mask, 256, H_kv=H_kv, window=window)
     rows = _rows(d, dt)
     load = [sum(max(2, key_blocks(qt, rows, N, mask, window)) + 1 for _, qt in wg) for wg in sched]
     mean = sum(load) / len(load)
@@ -119,29 +120,85 @@ def test_rounds_share_key_value_heads(N, H_kv, kv_per_round, heads_per_round):
             assert all(h // 4 == x for h in heads)  # the group's own heads
 
 
-def test_sliding_keeps_heads_fastest():
-    """Sliding windows number heads fastest: the short tiles at each head's
-    start land in the last rounds, spread over every workgroup."""
-    sched = fa.fa_fwd_schedule(1, 32, 32768, 128, BF16, SLIDING, 256)
+def _timeline(wg, rows, N, window):
+    """(start step, first key block, rank) of each tile of a workgroup, a tile
+    taking its key blocks (at least two) plus one step (its P V-only step);
+    the tile start and output cost the same for every tile."""
+    t, out = 0, []
+    for _, qt in wg:
+        lo = max(0, qt * rows - window + 1) // 64
+        out.append((t, lo, qt))
+        t += max(2, key_blocks(qt, rows, N, SLIDING, window)) + 1
+    return out
+
+
+@pytest.mark.parametrize("B,H,H_kv,N,window,cus,S",
+                         [(1, 32, 32, 32768, 4096, 256, 16), (1, 32, 8, 32768, 4096, 256, 16),
+                          (2, 32, 32, 16384, 2048, 256, 8), (1, 64, 64, 8192, 1024, 128, 4),
+                          (1, 12, 12, 8192, 1024, 24, 4)])
+def test_sliding_window_teams_stream_one_block(B, H, H_kv, N, window, cus, S):
+    """Windows of S row tiles: the group's workgroups form teams of S; once
+    each member has finished the first tile of a head (or before the last
+    one of an odd head), every member of a team reads the same key block at
+    the same step, and each member's load is the same."""
+    sched = fa.fa_fwd_schedule(B, H, N, 128, BF16, SLIDING, cus, H_kv=H_kv, window=window)
+    rows = 256
+    T = N // rows
+    G = len(sched)
+    n_groups = 8 if (B * H) % 8 == 0 else 1
+    J = G // n_groups
+    M = T // S
+    loads = set()
+    for x in range(n_groups):
+        members = [sched[gi] for gi in range(x, G, n_groups)]
+        for team in range(J // S):
+            lines = [_timeline(members[team * S + i], rows, N, window) for i in range(S)]
+            assert len({len(tl) for tl in lines}) == 1
+            for k in range(len(lines[0])):
+                hh, kk = divmod(k, M)
+                ramp = kk == 0 if hh % 2 == 0 else kk == M - 1
+                heads = {members[team * S + i][k][0] for i in range(S)}
+                assert len(heads) == 1  # one head per team at a time
+                if not ramp:
+                    # start step - first key block equal across the team
+                    assert len({t - lo for t, lo, _ in (tl[k] for tl in lines)}) == 1
+                else:
+                    assert all(tl[k][2] < S for tl in lines)
+            for i in range(S):
+                wg = members[team * S + i]
+                loads.add(sum(max(2, key_blocks(qt, rows, N, SLIDING, window)) + 1 for _, qt in wg))
+    assert len(loads) == 1
+
+
+@pytest.mark.parametrize("H,N,window", [(32, 32768, 4000), (32, 32768, 2048), (24, 32768, 4096),
+                                        (32, 32000, 4096)])
+def test_sliding_window_without_teams_keeps_heads_fastest(H, N, window):
+    """Windows that are not a whole number of row tiles, teams that would get
+    an odd number of heads, or N not a multiple of the row tile: heads
+    numbered fastest, the short tiles at each head's start in the last
+    rounds, spread over every workgroup."""
+    sched = fa.fa_fwd_schedule(1, H, N, 128, BF16, SLIDING, 256, window=window)
     first = [wg[0] for wg in sched]
-    assert len({bh for bh, _ in first}) == 32
-    assert all(qt >= 120 for _, qt in first)
+    T = -(-N // 256)
+    assert len({bh for bh, _ in first}) == min(H, len(sched))
+    assert all(qt >= T - 16 for _, qt in first)
 
 
 def test_schedule_rejects_bad_arguments():
     lib = fa.load()
     G, R = ctypes.c_int(0), ctypes.c_int(0)
     g, r = ctypes.byref(G), ctypes.byref(R)
-    assert lib.fa_fwd_schedule(0, 1, 1, 10, 128, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 1, 1, 10, 128, BF16, 7, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 1, 1, 10, 128, BF16, 0, 0, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 1, 1, 10, 100, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_UNSUPPORTED
-    assert lib.fa_fwd_schedule(1, 1, 1, 10, 128, 9, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 1, 1, 10, 128, BF16, 0, 256, None, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 1, 1, 1 << 30, 128, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 4, 3, 10, 128, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 4, 0, 10, 128, BF16, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(1, 2, 2, 1000, 128, BF16, 1, 256, g, r, None, 0) == fa.FA_OK
+    assert lib.fa_fwd_schedule(0, 1, 1, 10, 128, BF16, 0, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 1, 10, 128, BF16, 7, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 1, 10, 128, BF16, 0, 0, 0, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 1, 10, 100, BF16, 0, 0, 256, g, r, None, 0) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_fwd_schedule(1, 1, 1, 10, 128, 9, 0, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 1, 10, 128, BF16, 0, 0, 256, None, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 1, 1, 1 << 30, 128, BF16, 0, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 4, 3, 10, 128, BF16, 0, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 4, 0, 10, 128, BF16, 0, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_schedule(1, 2, 2, 1000, 128, BF16, 1, 0, 256, g, r, None, 0) == fa.FA_OK
+    assert lib.fa_fwd_schedule(1, 2, 2, 1000, 128, BF16, 2, 0, 256, g, r, None, 0) == fa.FA_ERR_INVALID_ARG
     buf = (ctypes.c_int * 4)()
-    assert lib.fa_fwd_schedule(1, 2, 2, 1000, 128, BF16, 1, 256, g, r,
+    assert lib.fa_fwd_schedule(1, 2, 2, 1000, 128, BF16, 1, 0, 256, g, r,
                                ctypes.cast(buf, ctypes.c_void_p), 4) == fa.FA_ERR_INVALID_ARG
