@@ -569,15 +569,21 @@ fa_fwd16_kernel(FaFwdParams p) {
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
         mx = pair_max(mx) * c2;  // block maximum of t (-inf: nothing visible)
         const float m_new = fmaxf(m_ref, mx == FA_NEG_INF ? FA_NEG_INF : m_use + mx);
-        const float alpha = m_new > m_ref ? (m_ref == FA_NEG_INF ? 0.f : exp2_hw(m_ref - m_new)) : 1.f;
+        // O and the sums are rescaled only where the reference rises above
+        // a finite one (a row that has seen no key holds zeros); the
+        // wavefront skips the multiplies when no lane needs them
+        const bool rise = m_new > m_ref && m_ref != FA_NEG_INF;
+        if (__ballot(rise)) {
+          const float alpha = rise ? exp2_hw(m_ref - m_new) : 1.f;
+          l_lane *= alpha;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) lsum[r] *= alpha;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+        }
         m_ref = m_new;
-        l_lane *= alpha;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lsum[r] *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
         const float shift = m_ref == FA_NEG_INF ? 0.f : m_use - m_ref;
         psum = 0.f;
 #pragma unroll
