@@ -666,10 +666,16 @@ fa_fwd16_kernel(FaFwdParams p) {
         if (p.tiles && kt < kv_end) record(kt, cls_cur);
       }
       phase_mfma(s, (s + 2) % 3);
+      // At d = 64 the matrix phase is the shorter half by far: a leading
+      // wave issues its K copies here, at the end of it (K slot (s+2) mod 3
+      // held block kt-1, whose last reader, the trailing waves' matrix
+      // phase kt-1, ended at the barrier before this phase), which takes
+      // them off the softmax half.
+      if (D == 64 && lead) issue_step(kt, s);
       __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
       barrier_nofence();
       phase_softmax(kt, cls_cur);
-      issue_step(kt, s);
+      if (D != 64 || !lead) issue_step(kt, s);
       wait_step(kt);
       __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
       barrier_nofence();
