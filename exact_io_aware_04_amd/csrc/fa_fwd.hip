@@ -299,8 +299,10 @@ __device__ __forceinline__ void matrix_phase(fa_f32x16 (&acc)[D / 32], fa_f32x16
 //
 // Persistent: one workgroup per compute unit walks its list of row tiles
 // (fa_persist_tile_of; under a causal mask or none, the tiles an XCD runs
-// together read one key/value head, so its L2 serves their common key and
-// value blocks once from HBM).  The K/V blocks of consecutive tiles form one stream
+// together read one key/value head, and under a sliding window of whole row
+// tiles each team of workgroups reads the same key/value block at the same
+// time, so the XCD's L2 serves their common key and value blocks once from
+// HBM).  The K/V blocks of consecutive tiles form one stream
 // through the LDS rings: the first two blocks of the next tile are loaded
 // during the last two steps of the current one, so a new tile starts with
 // its first blocks in LDS and no workgroup launch in between.

@@ -214,8 +214,9 @@ fa_fwd8_kernel(FaFwdParams p) {
 
   // Persistent: this workgroup's row tiles in the order of fa_persist_tile_of
   // (one workgroup per compute unit; under a causal mask or none, the tiles
-  // an XCD runs together read one key/value head, so its L2 serves their
-  // common key and value blocks).
+  // an XCD runs together read one key/value head, and under a sliding window
+  // of whole row tiles a team of workgroups reads one key/value block at a
+  // time, so the XCD's L2 serves their common key and value blocks).
   int bh, q0;
   for (int tile_k = 0; persist_tile(p, tile_k, bh, q0, ROWS_WG); ++tile_k) {
     const int q1 = min(q0 + ROWS_WG, N);
