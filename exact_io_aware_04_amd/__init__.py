@@ -24,6 +24,9 @@ import re
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfa.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "fa.h")
+# every header of the library: the method calls (fa.h) and the diagnostics
+# and host-side planners (fa_diag.h)
+HEADER_PATHS = (HEADER_PATH, os.path.join(os.path.dirname(_PKG), "include", "fa_diag.h"))
 
 FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16, FA_DTYPE_E4M3 = 0, 1, 2, 3
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_SLIDING = 0, 1, 2
@@ -91,8 +94,8 @@ def load():
 
 
 def declared_functions():
-    """Names of the functions include/fa.h declares."""
-    text = open(HEADER_PATH).read()
+    """Names of the functions include/fa.h and include/fa_diag.h declare."""
+    text = "".join(open(h).read() for h in HEADER_PATHS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 

@@ -14,6 +14,7 @@
 #include <string>
 
 #include "../../include/fa.h"
+#include "../../include/fa_diag.h"
 #include "fa_kernels.h"
 #include "tile_class.h"
 

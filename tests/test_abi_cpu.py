@@ -1,5 +1,6 @@
-"""The C-ABI library on the host: it loads, exports what include/fa.h
-declares, and rejects bad arguments before touching the device.
+"""The C-ABI library on the host: it loads, exports what include/fa.h and
+include/fa_diag.h declare, and rejects bad arguments before touching the
+device.
 
 Runs without a GPU.  Fake device addresses are plain integers that the
 library only compares and never dereferences: every call here either fails
@@ -28,9 +29,10 @@ def call(**kw):
 def test_library_loads_and_exports_every_declared_symbol():
     lib = fa.load()
     names = fa.declared_functions()
-    assert {"fa_fwd", "fa_fwd_gqa", "fa_fwd_fp8", "fa_bwd", "fa_decode", "fa_decode_workspace_bytes", "fa_fwd_record_tiles", "fa_tile_shape", "fa_tile_map",
-            "fa_status_string", "fa_last_error", "fa_probe_mfma", "fa_mfma_ceiling",
-            "fa_bwd_kv_parts"} <= set(names)
+    assert {"fa_fwd", "fa_fwd_gqa", "fa_fwd_fp8", "fa_bwd", "fa_bwd_gqa", "fa_decode",
+            "fa_decode_noalloc", "fa_decode_workspace_bytes", "fa_fwd_record_tiles",
+            "fa_tile_shape", "fa_tile_map", "fa_fwd_schedule", "fa_status_string",
+            "fa_last_error", "fa_probe_mfma", "fa_mfma_ceiling", "fa_bwd_kv_parts"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     # and they really are C symbols of the shared object
