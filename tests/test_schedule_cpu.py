@@ -135,7 +135,7 @@ def _timeline(wg, rows, N, window):
 @pytest.mark.parametrize("B,H,H_kv,N,window,cus,S",
                          [(1, 32, 32, 32768, 4096, 256, 16), (1, 32, 8, 32768, 4096, 256, 16),
                           (2, 32, 32, 16384, 2048, 256, 8), (1, 64, 64, 8192, 1024, 128, 4),
-                          (1, 12, 12, 8192, 1024, 24, 4)])
+                          (1, 12, 12, 8192, 1024, 24, 4), (1, 32, 32, 4096, 4096, 256, 16)])
 def test_sliding_window_teams_stream_one_block(B, H, H_kv, N, window, cus, S):
     """Windows of S row tiles: the group's workgroups form teams of S; once
     each member has finished the first tile of a head (or before the last
