@@ -125,7 +125,9 @@ __device__ __forceinline__ void load_block(const unsigned char* base, int r0, in
                                            FA_AS3 unsigned char* dst, int wave) {
   constexpr int ROWB = 2 * D, TILEB = BB * ROWB, LPW = TILEB / (NW * 1024);
   static_assert(LPW >= 1 && LPW * NW * 1024 == TILEB, "pieces must cover the block");
-  const int nb = max(min(N - r0, BB), 0) * ROWB;
+  // (wave-uniform, and held in scalar registers: a byte count left in a
+  // vector register makes the descriptor per-lane, and each load a loop)
+  const int nb = __builtin_amdgcn_readfirstlane(max(min(N - r0, BB), 0) * ROWB);
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(base + (r0 < N ? (size_t)r0 * ROWB : 0)), 0, nb, FA_BUF_WORD3);
 #pragma unroll
@@ -415,7 +417,8 @@ fa_bwd_dkdv_kernel(FaBwdParams p) {
       lse_next = r0 + lane < N ? lse_h[r0 + lane] : 0.f;
     } else if (wave == 1) {
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(dl_h + (r0 < N ? r0 : 0)), 0, max(min(N - r0, BB), 0) * 4, FA_BUF_WORD3);
+          (void*)(dl_h + (r0 < N ? r0 : 0)), 0,
+          __builtin_amdgcn_readfirstlane(max(min(N - r0, BB), 0) * 4), FA_BUF_WORD3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_AS3 void*)&dl[b][0], 4, lane * 4, 0, 0, 0);
     }
   };
