@@ -455,7 +455,8 @@ fa_fwd16_kernel(FaFwdParams p) {
   // loaded, and their first P V product reads the previous tile's last V
   // block (finite values, times probability 0).
   issue(lead ? cur.Kh : cur.Vh, my_off, lead ? kbuf(0) : vbuf(0), cur.kv_lo);
-  issue(lead ? cur.Kh : cur.Vh, my_off, lead ? kbuf(1) : vbuf(1), cur.kv_lo + 1);
+  // (at d = 64 the second V block is loaded by the first step)
+  if (D != 64 || lead) issue(lead ? cur.Kh : cur.Vh, my_off, lead ? kbuf(1) : vbuf(1), cur.kv_lo + 1);
 #pragma unroll
   for (int i = 0; i < TILEB / (NW * 64 * 16); ++i)
     *(FA_AS3 fa_u32x4*)(vbuf(2) + (i * NW * 64 + tid) * 16) = fa_u32x4{0u, 0u, 0u, 0u};
@@ -645,6 +646,44 @@ fa_fwd16_kernel(FaFwdParams p) {
       else
         __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
     };
+    // At d = 64 the matrix phase is the shorter half by far (half the
+    // products of d = 128 beside the same softmax), so the copies leave
+    // the softmax half altogether: at the end of its matrix phase kt a
+    // leading wave issues its shares of both V(kt+1), into the V slot of
+    // block kt-2 (last read by matrix phase kt-1 of both groups, which
+    // ended at the barrier before this phase), and K(kt+2), into the K slot
+    // of block kt-1 (last read by the trailing waves' matrix phase kt-1),
+    // then waits for its copies of the previous step, which matrix phase
+    // kt+1 reads first.  The trailing waves copy nothing.  In the V stream
+    // position kt+1 is this tile's block or, for kt = kv_hi-1, the next
+    // tile's first; the next tile's second is loaded by its own first step.
+    // On a later tile's first step the K slot being replaced holds the
+    // leading waves' staged output of the previous tile, which they may
+    // still be reading back, so that K copy waits for the barrier that
+    // ends the phase (and the next matrix phase's wait covers it).
+    const unsigned char* k_cur = uniform_ptr(cur.Kh);
+    const unsigned char* k_nxt = uniform_ptr(nxt.Kh);
+    const unsigned char* v_cur = uniform_ptr(cur.Vh);
+    const unsigned char* v_nxt = uniform_ptr(nxt.Vh);
+    auto issue_k64 = [&](int kt, int s) {
+      const bool here = kt + 2 < kv_hi;
+      issue(here ? k_cur : k_nxt, koff, kbuf((s + 2) % 3), here ? kt + 2 : nxt_lo + (kt + 2 - kv_hi));
+    };
+    auto matrix_end64 = [&](int kt, int s) {
+      const bool iv = kt + 1 < kv_hi || (kt < kv_hi && has_next);
+      const bool ik = issued(kt) && !(kt == kv_lo && tile_k > 0);
+      if (iv) {
+        const bool here = kt + 1 < kv_hi;
+        issue(here ? v_cur : v_nxt, voff, vbuf((s + 1) % 3), here ? kt + 1 : nxt_lo);
+      }
+      if (ik) issue_k64(kt, s);
+      if (iv && ik)
+        __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(2 * LPW));
+      else if (iv || ik)
+        __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(LPW));
+      else
+        __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
+    };
 
     // Every wave runs, for kt = kv_lo .. kv_hi: matrix phase kt (scores of
     // block kt, P V of block kt-1), barrier, softmax phase kt, barrier.  The
@@ -659,6 +698,7 @@ fa_fwd16_kernel(FaFwdParams p) {
     // replace (lgkmcnt(0) before each barrier); K(kt+1) and V(kt+1), issued
     // in the previous step, are waited for before the barriers that end
     // h + 1 and h + 2, ahead of matrix phases kt+1 and kt+2 that read them.
+    // (d = 64: the leading waves' copies at the end of h, described above.)
     // Tiles follow each other with the same barrier count in both groups.
     auto step = [&](int kt, int s) {
       int cls_cur = FA_TILE_FULL;
@@ -668,17 +708,16 @@ fa_fwd16_kernel(FaFwdParams p) {
         if (p.tiles && kt < kv_end) record(kt, cls_cur);
       }
       phase_mfma(s, (s + 2) % 3);
-      // At d = 64 the matrix phase is the shorter half by far: a leading
-      // wave issues its K copies here, at the end of it (K slot (s+2) mod 3
-      // held block kt-1, whose last reader, the trailing waves' matrix
-      // phase kt-1, ended at the barrier before this phase), which takes
-      // them off the softmax half.
-      if (D == 64 && lead) issue_step(kt, s);
+      if (D == 64 && lead) matrix_end64(kt, s);
       __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
       barrier_nofence();
       phase_softmax(kt, cls_cur);
-      if (D != 64 || !lead) issue_step(kt, s);
-      wait_step(kt);
+      if constexpr (D == 64) {
+        if (lead && kt == kv_lo && tile_k > 0 && issued(kt)) issue_k64(kt, s);
+      } else {
+        issue_step(kt, s);
+        wait_step(kt);
+      }
       __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
       barrier_nofence();
     };
@@ -717,9 +756,10 @@ fa_fwd16_kernel(FaFwdParams p) {
       // Scratch for the restaged output: ring slot (ph + kv_hi - kv_lo + 2)
       // mod 3, which holds this tile's last block -- K no longer read, V
       // read next only by the next tile's first step, with probability 0
-      // (any finite values do) -- and is refilled only at the end of that
-      // step's softmax phase.  Waves 0-3 use the K slot, 4-7 the V slot,
-      // 16 rows each (4 KB at d = 128, 2 KB at d = 64: a slot holds 64 rows).
+      // (any finite values do) -- and is refilled no earlier than the end
+      // of that step's softmax phase.  Waves 0-3 use the K slot, 4-7 the V
+      // slot, 16 rows each (4 KB at d = 128, 2 KB at d = 64: a slot holds 64
+      // rows).
       static_assert(NL * 16 * ROWB <= TILEB, "four 16-row stages must fit in one slot");
       const int sl = (ph + (kv_hi - kv_lo) + 2) % 3;
       FA_AS3 unsigned char* stage = (lead ? kbuf(sl) : vbuf(sl)) + (wave % NL) * (16 * ROWB);
