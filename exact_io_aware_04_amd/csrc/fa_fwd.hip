@@ -21,7 +21,9 @@
 //    the LDS destination: no VGPR staging, no VALU) into rings of three
 //    slots each; block kt+2 is loaded while block kt is computed, K by the
 //    leading and V by the trailing wavefronts, each at the end of its
-//    softmax phase.  The buffer descriptor of each block ends at key N, so
+//    softmax phase (at d = 64, where the matrix phase is the shorter half,
+//    the leading wavefronts load both at the end of their matrix phase).
+//    The buffer descriptor of each block ends at key N, so
 //    keys past the end read as zeros.  Rows are stored with an XOR swizzle of
 //    their 16-byte chunks (applied on the global side, since the LDS side of
 //    these loads is lane-contiguous) so that both LDS read patterns below
@@ -616,8 +618,8 @@ fa_fwd16_kernel(FaFwdParams p) {
 
     // Loads.  The blocks of this tile and the next form one stream through
     // the rings: block kt of this tile lives in slot (ph + kt - kv_lo) mod
-    // 3, the next tile's first block in slot (ph + kv_hi - kv_lo) mod 3.  At
-    // the end of its softmax phase kt (where it would otherwise wait at the
+    // 3, the next tile's first block in slot (ph + kv_hi - kv_lo) mod 3.
+    // For d = 128 (d = 64: below): at the end of its softmax phase kt (where it would otherwise wait at the
     // barrier) a leading wave issues its share of the K block two places
     // further in the stream, a trailing wave its share of that V block, into
     // the slots of block kt-1, whose last reader (matrix phase kt-1 for K,
