@@ -175,6 +175,27 @@ def test_ragged_sizes(dtype, d, mask, window):
             compare(o, lse, o_ref, lse_ref, dt, "N=%d dtype-out" % N)
 
 
+# ---------------------------------------------------------------------------
+# many short row tiles per persistent workgroup: every workgroup runs two to
+# four tiles back to back, so the key/value stream crosses tile boundaries
+# between tiles of two blocks (the shortest; at N = 50 the second lies
+# wholly past N) and, under the masks, tiles of different lengths
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 100)])
+@pytest.mark.parametrize("B,H,N", [(8, 100, 50), (4, 160, 100), (2, 200, 300), (1, 300, 600)])
+def test_many_tiles_per_workgroup(dtype, d, mask, window, B, H, N):
+    dt = DT[dtype]
+    say("many tiles", dtype, d, mask, window, B, H, N)
+    q, k, v = si.make_qkv(B, H, N, d, dtype, 7400 + N + d + H)
+    scale = 1.0 / math.sqrt(d)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, mask, window)
+    o, lse = run(q, k, v, scale, mask, window, torch.float32)
+    compare(o, lse, o_ref, lse_ref, dt, "B=%d H=%d N=%d fp32-out" % (B, H, N))
+    o, lse = run(q, k, v, scale, mask, window)
+    compare(o, lse, o_ref, lse_ref, dt, "B=%d H=%d N=%d dtype-out" % (B, H, N))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [128, 256])
 def test_large_logits_stress(dtype, d):
