@@ -324,6 +324,10 @@ fa_fwd16_kernel(FaFwdParams p) {
   static_assert(LPW * NL * 1024 == TILEB, "loads must cover the block");
   static_assert(NL * 1024 / ROWB % 16 == 0, "pieces must be a multiple of 16 rows apart");
   static_assert(NW == 8 && FA_STAGES_16 == 3, "schedule below: 2 x 4 wavefronts, rings of 3");
+  // One workgroup barrier per key block at d = 64 (where the softmax phase
+  // takes about twice as long as the matrix phase), two at d = 128; the
+  // step loop below describes both schedules.
+  constexpr bool ONE_BARRIER = D == 64;
   // LDS: rings of three K and three V blocks, as separate objects so that
   // the compiler can tell the slots being read from the ones being filled
   // (and does not wait for the prefetches before reading)
@@ -560,7 +564,7 @@ fa_fwd16_kernel(FaFwdParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             pr[kb][r] = exp2_hw(sc[kb][r] * c2);
-            psum += pr[kb][r];
+            psum = kb == 0 && r == 0 ? pr[kb][r] : psum + pr[kb][r];  // (no 0 + p)
           }
         exact = __ballot(!(psum <= 256.f));
       }
@@ -596,7 +600,7 @@ fa_fwd16_kernel(FaFwdParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             pr[kb][r] = exp2_hw(__builtin_fmaf(sc[kb][r], c2, shift));
-            psum += pr[kb][r];
+            psum = kb == 0 && r == 0 ? pr[kb][r] : psum + pr[kb][r];  // (no 0 + p)
           }
         const float mn = m_ref == FA_NEG_INF ? 0.f : -m_ref * inv_c2;
 #pragma unroll
@@ -653,16 +657,13 @@ fa_fwd16_kernel(FaFwdParams p) {
     // the softmax half altogether: at the end of its matrix phase kt a
     // leading wave issues its shares of both V(kt+1), into the V slot of
     // block kt-2 (last read by matrix phase kt-1 of both groups, which
-    // ended at the barrier before this phase), and K(kt+2), into the K slot
+    // ended at a barrier before this phase), and K(kt+2), into the K slot
     // of block kt-1 (last read by the trailing waves' matrix phase kt-1),
     // then waits for its copies of the previous step, which matrix phase
     // kt+1 reads first.  The trailing waves copy nothing.  In the V stream
     // position kt+1 is this tile's block or, for kt = kv_hi-1, the next
     // tile's first; the next tile's second is loaded by its own first step.
-    // On a later tile's first step the K slot being replaced holds the
-    // leading waves' staged output of the previous tile, which they may
-    // still be reading back, so that K copy waits for the barrier that
-    // ends the phase (and the next matrix phase's wait covers it).
+    // (A later tile's first K copy waits for a barrier: see the step loop.)
     const unsigned char* k_cur = uniform_ptr(cur.Kh);
     const unsigned char* k_nxt = uniform_ptr(nxt.Kh);
     const unsigned char* v_cur = uniform_ptr(cur.Vh);
@@ -687,8 +688,10 @@ fa_fwd16_kernel(FaFwdParams p) {
         __builtin_amdgcn_s_waitcnt(FA_WAITCNT_VM_LGKM0(0));
     };
 
-    // Every wave runs, for kt = kv_lo .. kv_hi: matrix phase kt (scores of
-    // block kt, P V of block kt-1), barrier, softmax phase kt, barrier.  The
+    // Every wave runs, for kt = kv_lo .. kv_hi, matrix phase kt (scores of
+    // block kt, P V of block kt-1) and softmax phase kt.
+    //
+    // d = 128: two workgroup barriers per step, one after each phase.  The
     // trailing waves pass one barrier before their first step, the leading
     // ones one after their last, so a trailing wave's matrix phase kt runs
     // beside the leading waves' softmax phase kt, and its softmax phase kt
@@ -700,7 +703,26 @@ fa_fwd16_kernel(FaFwdParams p) {
     // replace (lgkmcnt(0) before each barrier); K(kt+1) and V(kt+1), issued
     // in the previous step, are waited for before the barriers that end
     // h + 1 and h + 2, ahead of matrix phases kt+1 and kt+2 that read them.
-    // (d = 64: the leading waves' copies at the end of h, described above.)
+    //
+    // d = 64 (ONE_BARRIER): one barrier per step, after the softmax phase in
+    // a leading wave and between the two phases in a trailing one.  In
+    // interval I(kt) (between the barriers of steps kt-1 and kt) a leading
+    // wave runs matrix phase kt and then softmax phase kt, a trailing wave
+    // softmax phase kt-1 and then matrix phase kt: program order keeps the
+    // two waves of a SIMD in opposite phases, and since the softmax is the
+    // longer phase by far at d = 64, a leading wave starts its softmax as
+    // soon as its products are issued instead of waiting at a barrier for
+    // its partner's softmax.  The copies (issued at the end of a leading
+    // wave's matrix phase, described above) keep their slots: V(kt+1) goes
+    // into the slot of V(kt-2), last read in I(kt-1), K(kt+2) into that of
+    // K(kt-1), also last read in I(kt-1); the wait that follows covers the
+    // copies of step kt-1, read from I(kt+1) on.  On a later tile's first
+    // step the K slot being replaced holds the leading waves' staged output
+    // of the previous tile, which the other leading waves may still be
+    // reading back: that copy is issued at the start of the next step,
+    // after the barrier, and the next step's wait covers it.  On a tile's
+    // first step both groups start with a matrix phase.
+    //
     // Tiles follow each other with the same barrier count in both groups.
     auto step = [&](int kt, int s) {
       int cls_cur = FA_TILE_FULL;
@@ -709,24 +731,29 @@ fa_fwd16_kernel(FaFwdParams p) {
                               : FA_TILE_SKIP;
         if (p.tiles && kt < kv_end) record(kt, cls_cur);
       }
+      if constexpr (ONE_BARRIER) {
+        if (lead && tile_k > 0 && kt == kv_lo + 1 && issued(kv_lo)) issue_k64(kv_lo, (s + 2) % 3);
+      }
       phase_mfma(s, (s + 2) % 3);
       if (D == 64 && lead) matrix_end64(kt, s);
-      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
-      barrier_nofence();
+      if (!ONE_BARRIER || !lead) {
+        __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
+        barrier_nofence();
+      }
       phase_softmax(kt, cls_cur);
-      if constexpr (D == 64) {
-        if (lead && kt == kv_lo && tile_k > 0 && issued(kt)) issue_k64(kt, s);
-      } else {
+      if constexpr (D != 64) {
         issue_step(kt, s);
         wait_step(kt);
       }
-      __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
-      barrier_nofence();
+      if (!ONE_BARRIER || lead) {
+        __builtin_amdgcn_s_waitcnt(FA_WAITCNT_LGKM0);
+        barrier_nofence();
+      }
     };
 
     if (p.tiles)
       for (int kt = full_lo; kt < full_hi; ++kt) record(kt, FA_TILE_FULL);
-    if (!lead) barrier_nofence();
+    if (!ONE_BARRIER && !lead) barrier_nofence();
     // steps kt = kv_lo .. kv_hi; step kt uses ring slot (ph + kt - kv_lo)
     // mod 3 (entered at the slot of the tile's first block)
     {
@@ -746,12 +773,13 @@ fa_fwd16_kernel(FaFwdParams p) {
         entry = 0;
       }
     }
-    // The next tile's Q rows: loaded before the leading waves' last barrier
-    // (where they wait for the trailing waves' last softmax phase), and
-    // before this tile's output is stored.  (A load inside the step loop
-    // would make the compiler wait for it before every score product.)
+    // The next tile's Q rows: loaded before this tile's output is stored
+    // (and, with two barriers per step, before the leading waves' last
+    // barrier, where they wait for the trailing waves' last softmax phase).
+    // A load inside the step loop would make the compiler wait for it
+    // before every score product.
     if (has_next) load_q(nxt.bh, nxt.q0);
-    if (lead) barrier_nofence();
+    if (!ONE_BARRIER && lead) barrier_nofence();
     if constexpr (OUT_F32) {
       store_output<DT, D, OUT_F32>(p, acc, m_ref, pair_sum(l_lane), lsum[0], bh, qi, half);
     } else {
