@@ -225,6 +225,29 @@ __device__ __forceinline__ fa_f32x4 rowsum_mma(fa_u32x4 sel, fa_u32x4 b, fa_f32x
         __builtin_bit_cast(fa_f16x8, sel), __builtin_bit_cast(fa_f16x8, b), c, 0, 0, 0);
 }
 
+// Largest of a block's rounded fp16 probabilities, as its bit pattern:
+// non-negative fp16 values order like their bits, and infinity and NaN
+// sort above every finite value.  Packed 16-bit maxima, then the larger
+// half.
+#define FA_F16_BITS_256 0x5C00u  // 256.0 in fp16
+typedef unsigned short fa_u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ fa_u16x2 u16_pair(unsigned w) { return __builtin_bit_cast(fa_u16x2, w); }
+__device__ __forceinline__ fa_u16x2 u16_max(fa_u16x2 a, fa_u16x2 b) {
+  return __builtin_elementwise_max(a, b);
+}
+__device__ __forceinline__ unsigned max_f16_bits(const fa_u32x4 (&pf)[2][2]) {
+  // (each word is read into a scalar first: hipcc took element 0 for every
+  // index when the vector element went to __builtin_bit_cast directly)
+  fa_u16x2 m[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned a = pf[0][0][i], b = pf[0][1][i], c = pf[1][0][i], d = pf[1][1][i];
+    m[i] = u16_max(u16_max(u16_pair(a), u16_pair(b)), u16_max(u16_pair(c), u16_pair(d)));
+  }
+  const fa_u16x2 r = u16_max(u16_max(m[0], m[1]), u16_max(m[2], m[3]));
+  return max((unsigned)r.x, (unsigned)r.y);
+}
+
 // Matrix phase of one wavefront: S^T = K Q^T over the current key block (QK)
 // and O^T += V^T P^T over the previous one (PV), as one software-pipelined
 // sequence of products whose LDS operands are read FA_OPND_AHEAD products
@@ -328,6 +351,9 @@ fa_fwd16_kernel(FaFwdParams p) {
   // takes about twice as long as the matrix phase), two at d = 128; the
   // step loop below describes both schedules.
   constexpr bool ONE_BARRIER = D == 64;
+  // fp16 inputs: lse from the sum of the rounded probabilities (see the
+  // softmax phase), and no unrounded sum.
+  constexpr bool F16_SUMS = DT == 1;
   // LDS: rings of three K and three V blocks, as separate objects so that
   // the compiler can tell the slots being read from the ones being filled
   // (and does not wait for the prefetches before reading)
@@ -559,14 +585,34 @@ fa_fwd16_kernel(FaFwdParams p) {
       float psum = 0.f;
       bool exact = cls == FA_TILE_PARTIAL || __ballot(m_ref == FA_NEG_INF);
       if (!exact) {
+        if constexpr (F16_SUMS) {
+          // fp16: the probabilities are rounded first and the largest of
+          // them bounds the block (no unrounded sum is needed)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            pr[kb][r] = exp2_hw(sc[kb][r] * c2);
-            psum = kb == 0 && r == 0 ? pr[kb][r] : psum + pr[kb][r];  // (no 0 + p)
-          }
-        exact = __ballot(!(psum <= 256.f));
+            for (int r = 0; r < 16; ++r) pr[kb][r] = exp2_hw(sc[kb][r] * c2);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              pf[kb][t] = pack8<DT>(&pr[kb][8 * t]);
+              // (an empty statement that makes the packed words opaque, so
+              // that the maximum reads the registers the products read
+              // instead of converting every probability a second time)
+              asm("" : "+v"(pf[kb][t]));
+            }
+          exact = __ballot(max_f16_bits(pf) > FA_F16_BITS_256);
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              pr[kb][r] = exp2_hw(sc[kb][r] * c2);
+              psum = kb == 0 && r == 0 ? pr[kb][r] : psum + pr[kb][r];  // (no 0 + p)
+            }
+          exact = __ballot(!(psum <= 256.f));
+        }
       }
       if (exact) {
         if (cls == FA_TILE_PARTIAL) apply_mask<NKB>(sc, kt * BC, qi, half, N, p.mask_kind, p.window);
@@ -600,24 +646,27 @@ fa_fwd16_kernel(FaFwdParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             pr[kb][r] = exp2_hw(__builtin_fmaf(sc[kb][r], c2, shift));
-            psum = kb == 0 && r == 0 ? pr[kb][r] : psum + pr[kb][r];  // (no 0 + p)
+            if constexpr (!F16_SUMS) psum = kb == 0 && r == 0 ? pr[kb][r] : psum + pr[kb][r];
           }
         const float mn = m_ref == FA_NEG_INF ? 0.f : -m_ref * inv_c2;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc0[r] = mn;
       }
-      // Two row sums.  The output is normalised by the sum of the ROUNDED
+      // Row sums.  The output is normalised by the sum of the ROUNDED
       // probabilities (the values the matrix core multiplies V with; summed
       // on the matrix core in the next matrix phase), so output and
       // normaliser use identical weights: constant V comes out exact and a
-      // dominant key is selected exactly.  lse uses the sum of the unrounded
-      // probabilities, which rounding to 16 bits would otherwise move by up
-      // to 2^-9.
+      // dominant key is selected exactly.  With bf16 inputs lse uses the sum
+      // of the unrounded probabilities, which rounding to bf16 would move by
+      // up to 2^-9 (relative); fp16 rounding moves it by at most 2^-11, so
+      // with fp16 inputs lse comes from the rounded sum as well.
+      if (!F16_SUMS || exact) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) pf[kb][t] = pack8<DT>(&pr[kb][8 * t]);
-      l_lane += psum;
+          for (int t = 0; t < 2; ++t) pf[kb][t] = pack8<DT>(&pr[kb][8 * t]);
+      }
+      if constexpr (!F16_SUMS) l_lane += psum;
     };
 
     // Loads.  The blocks of this tile and the next form one stream through
@@ -781,7 +830,7 @@ fa_fwd16_kernel(FaFwdParams p) {
     if (has_next) load_q(nxt.bh, nxt.q0);
     if (!ONE_BARRIER && lead) barrier_nofence();
     if constexpr (OUT_F32) {
-      store_output<DT, D, OUT_F32>(p, acc, m_ref, pair_sum(l_lane), lsum[0], bh, qi, half);
+      store_output<DT, D, OUT_F32>(p, acc, m_ref, F16_SUMS ? lsum[0] : pair_sum(l_lane), lsum[0], bh, qi, half);
     } else {
       // Scratch for the restaged output: ring slot (ph + kv_hi - kv_lo + 2)
       // mod 3, which holds this tile's last block -- K no longer read, V
@@ -793,7 +842,8 @@ fa_fwd16_kernel(FaFwdParams p) {
       static_assert(NL * 16 * ROWB <= TILEB, "four 16-row stages must fit in one slot");
       const int sl = (ph + (kv_hi - kv_lo) + 2) % 3;
       FA_AS3 unsigned char* stage = (lead ? kbuf(sl) : vbuf(sl)) + (wave % NL) * (16 * ROWB);
-      store_output_staged<DT, D>(p, acc, m_ref, pair_sum(l_lane), lsum[0], bh, qb0, lane, stage);
+      store_output_staged<DT, D>(p, acc, m_ref, F16_SUMS ? lsum[0] : pair_sum(l_lane), lsum[0], bh, qb0,
+                                 lane, stage);
     }
 
     if (!has_next) break;
