@@ -83,7 +83,11 @@ enum {
  *   stream     hipStream_t or NULL
  * Arithmetic: products on the matrix cores in the input precision with fp32
  * accumulation; softmax statistics in fp32; probabilities are rounded to the
- * input precision (round to nearest even) before the product with V.
+ * input precision (round to nearest even) before the product with V, and O is
+ * divided by the sum of those rounded weights.  lse uses the sum of the
+ * unrounded probabilities with bf16 inputs and the sum of the rounded ones
+ * with fp16 inputs (fp16 rounding moves it by at most 2^-11 relative, i.e.
+ * lse by at most 4.9e-4).
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int mask_kind, int window,
