@@ -115,6 +115,26 @@ def test_workload_whole_tensor(w):
         say("%s dtype-out: max|dO| %.3g max|dlse| %.3g" % (w.name, eo, el))
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("d,mask,logit_x", [(64, "none", 1), (128, "causal", 1), (128, "causal", 4)])
+def test_f16_lse_from_rounded_sums_long_rows(d, mask, logit_x):
+    """fp16 inputs take lse from the sum of the fp16-rounded probabilities
+    (each moved by at most 2^-11 of itself, so lse by at most 4.9e-4): every
+    element of O and lse over rows of up to 16384 keys, with the plain scale
+    and with logits four times larger (rows dominated by a few keys), against
+    the fp64 oracle at the stated tolerances (lse 1e-3)."""
+    B, H, N = 1, 2, 16384
+    scale = logit_x / math.sqrt(d)
+    q, k, v = si.make_qkv(B, H, N, d, "f16", 9300 + d + logit_x)
+    say("f16 lse long rows", d, mask, logit_x, "gpu")
+    o, lse = run(q, k, v, scale, mask, 0)
+    o, lse = o.cpu(), lse.cpu()
+    say("f16 lse long rows", d, mask, logit_x, "oracle")
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, mask, 0)
+    eo, el = compare(o, lse, o_ref, lse_ref, torch.float16, "f16 long rows d=%d %s x%d" % (d, mask, logit_x))
+    say("f16 long rows d=%d %s x%d: max|dO| %.3g max|dlse| %.3g" % (d, mask, logit_x, eo, el))
+
+
 def sample_rows(N, rng, extra=64):
     fixed = list(range(0, 64)) + [127, 128, 129, 4095, 4096, 4097, N // 2, N // 2 + 1]
     fixed += list(range(N - 64, N))
